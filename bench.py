@@ -1,0 +1,208 @@
+"""Benchmark of the software-pipelined tiled GEMM on one MI355X.
+
+One step = one C = A . B call on the headline workload (FP16 inputs, FP32
+accumulate, M = N = K = 4096) with the operands already resident in HBM.
+Timing uses HIP events recorded on the stream the kernels are launched on
+(torch's current stream), bracketing exactly --steps launches after
+--warmup untimed ones ("Analyze Kernel Bottleneck", Step 1: event timing
+after warm-up, effective GFLOPS = 2*M*N*K / t).
+
+Printed: ONE JSON line with the headline value, a roofline object for the
+kernel, the CPU oracle timed on a bounded sample on this host's cores, and a
+side-by-side table of every workload x loop variant (single-buffer,
+register prefetch, direct-to-LDS).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synthetic_inputs as si  # noqa: E402
+
+METRIC = "GEMM TFLOPS/TOPS at 4096³ (FP16, INT8) + % of MFMA peak; skinny GB/s % HBM"
+PEAK = {"f16": 2500.0, "i8": 5000.0}   # dense MFMA, TFLOP/s and TOP/s
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="fp16_4096", choices=sorted(si.WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-table", action="store_true", help="skip the per-workload variant table")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="also run one device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def device_operands(wl):
+    import torch
+    A, B = wl.operands()
+    if wl.dtype == "f16":
+        dA = torch.from_numpy(A.view(np.int16)).cuda().view(torch.float16)
+        dB = torch.from_numpy(B.view(np.int16)).cuda().view(torch.float16)
+        C = torch.empty((wl.M, wl.N), dtype=torch.float32, device="cuda")
+    else:
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        C = torch.empty((wl.M, wl.N), dtype=torch.int32, device="cuda")
+    return A, B, dA, dB, C
+
+
+def launcher(tdg, wl, dA, dB, C, variant: str):
+    f16 = wl.dtype == "f16"
+    if variant == "pipelined":
+        fn = tdg.gemm_f16f32_pipelined if f16 else tdg.gemm_i8i32_pipelined
+        return lambda: fn(dA, dB, C)
+    if variant == "single":
+        fn = tdg.gemm_f16f32 if f16 else tdg.gemm_i8i32
+        return lambda: fn(dA, dB, C)
+    cfg = {"reg_s1": dict(variant=tdg.TDG_VARIANT_REG_PREFETCH, lds_stages=1),
+           "reg_s2": dict(variant=tdg.TDG_VARIANT_REG_PREFETCH, lds_stages=2),
+           "direct": dict(variant=tdg.TDG_VARIANT_DIRECT_LDS, lds_stages=2)}[variant]
+    fn = tdg.gemm_f16f32_ex if f16 else tdg.gemm_i8i32_ex
+    return lambda: fn(dA, dB, C, cfg=cfg)
+
+
+def time_launches(run, steps: int, warmup: int) -> float:
+    """Mean milliseconds per launch over `steps` back-to-back launches,
+    bracketed by events on the launching (current) stream."""
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def throughput(wl, ms: float):
+    ops = 2.0 * wl.M * wl.N * wl.K
+    es = 2 if wl.dtype == "f16" else 1
+    alg_bytes = (wl.M * wl.K + wl.K * wl.N) * es + wl.M * wl.N * 4
+    return ops / (ms * 1e-3) / 1e12, alg_bytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(wl, A, B, target_s: float):
+    """The oracle as it stands, on a bounded sample: the first R rows of C,
+    R chosen so the run takes about target_s seconds on this host."""
+    import oracle
+    threads = oracle.host_threads()
+    fn = oracle.gemm_f16 if wl.dtype == "f16" else oracle.gemm_i8
+    probe_rows = max(threads, 16)
+    t0 = time.perf_counter()
+    fn(A[:probe_rows], B, threads=threads)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(wl.M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
+    rows = max(threads, (rows // threads) * threads)
+    t0 = time.perf_counter()
+    fn(A[:rows], B, threads=threads)
+    secs = time.perf_counter() - t0
+    tops = 2.0 * rows * wl.N * wl.K / secs / 1e12
+    unit = "TFLOP/s" if wl.dtype == "f16" else "TOP/s"
+    return {"value": tops, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": "rows 0..%d of C (%d x %d x %d, %.1f s)" % (rows - 1, rows, wl.N, wl.K, secs)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tiled_dense_gemm_loop_amd as tdg
+    tdg.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    wl = si.WORKLOADS[args.workload]
+    A, B, dA, dB, C = device_operands(wl)
+    run = launcher(tdg, wl, dA, dB, C, "pipelined")
+    ms = time_launches(run, args.steps, args.warmup)
+    tops, gbs = throughput(wl, ms)
+    dcode = tdg.TDG_DTYPE_F16F32 if wl.dtype == "f16" else tdg.TDG_DTYPE_I8I32
+    cfg, info = tdg.tdg_plan(dcode, wl.M, wl.N, wl.K)
+    unit = "TFLOP/s" if wl.dtype == "f16" else "TOP/s"
+    print("# %s pipelined (%s, %dx%dx%d, %d waves): %.4f ms/launch, %.1f %s"
+          % (wl.name, tdg.VARIANT_NAMES[cfg["variant"]], cfg["bm"], cfg["bn"], cfg["bk"],
+             cfg["waves"], ms, tops, unit), file=sys.stderr, flush=True)
+
+    table = {}
+    if not args.no_table:
+        for name, w in si.WORKLOADS.items():
+            if name == wl.name:
+                a, b, da, db, c = A, B, dA, dB, C
+            else:
+                a, b, da, db, c = device_operands(w)
+            row = {}
+            for variant in ("single", "reg_s1", "reg_s2", "direct", "pipelined"):
+                t = time_launches(launcher(tdg, w, da, db, c, variant), 20, 3)
+                tp, bw = throughput(w, t)
+                row[variant] = {"us": round(t * 1e3, 2), "tops": round(tp, 1), "gbs": round(bw, 1)}
+            row["speedup_pipelined_vs_single"] = round(row["single"]["us"] / row["pipelined"]["us"], 3)
+            table[name] = row
+            print("# %-12s %s" % (name, json.dumps(row)), file=sys.stderr, flush=True)
+            if name != wl.name:
+                del a, b, da, db, c
+                torch.cuda.empty_cache()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, A, B, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
+                   "accumulate": "f32" if wl.dtype == "f16" else "i32",
+                   "kernel": "%dx%dx%d tile, %d waves, %d LDS stages, %s" % (
+                       cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
+                       tdg.VARIANT_NAMES[cfg["variant"]]),
+                   "parallelism": "none"},
+        "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK[wl.dtype],
+                     "unit": unit, "frac": round(tops / PEAK[wl.dtype], 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "variants": table or None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

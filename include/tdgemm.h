@@ -1,0 +1,150 @@
+/*
+ * tdgemm.h -- C ABI of the MI355X (gfx950) tiled dense GEMM library.
+ *
+ * Every entry point computes C = A . B, the plain matrix product ("Pipeline
+ * GPU Kernel", Step 2: 2 operations per multiply-add; "Analyze Kernel
+ * Bottleneck", Step 1: a GEMM does 2*M*N*K operations), with
+ *   A: M x K, row-major, leading dimension lda (elements),
+ *   B: K x N, row-major, leading dimension ldb (elements),
+ *   C: M x N, row-major, leading dimension ldc (elements), overwritten.
+ * FP16 entry points take binary16 inputs as raw 16-bit patterns and write
+ * FP32 results accumulated in FP32; INT8 entry points take int8 inputs and
+ * write INT32 results accumulated in INT32 (exact while |C| < 2^31, which
+ * holds for every K <= 131071).
+ *
+ * The K loop runs in tiles of BK elements staged through on-chip LDS:
+ *   - the unpipelined entry points run the sequential baseline: load tile t,
+ *     barrier, compute on it, barrier ("Pipeline GPU Kernel", Step 1);
+ *   - the _pipelined entry points run the prologue / main loop / epilogue
+ *     form in which the global load of tile t+1 is in flight while the matrix
+ *     cores compute on tile t, with two LDS buffers ("Pipeline GPU Kernel",
+ *     Step 3 and Step 4).  The variant (register prefetch or direct
+ *     global-to-LDS) is chosen per shape by tdg_plan.
+ *
+ * Pointers A, B, C are DEVICE pointers owned by the caller; the library never
+ * allocates, frees or synchronises.  `stream` is a hipStream_t (NULL = the
+ * null stream); each call only enqueues work and returns.  Calls are
+ * thread-safe.
+ *
+ * Argument rules (violations return TDG_ERR_INVALID_ARG before any HIP call):
+ *   M, N, K >= 0;  lda >= max(1, K);  ldb >= max(1, N);  ldc >= max(1, N);
+ *   a pointer may be NULL only when its matrix is empty;
+ *   the bytes C spans may not overlap those of A or B.
+ * Degenerate shapes: M == 0 or N == 0 returns TDG_OK and launches nothing;
+ * K == 0 writes zeros to C.
+ * Any shape and alignment is accepted.  The fast path needs 16-byte aligned
+ * A and B, lda and ldb whole multiples of 16 bytes and M, N, K whole multiples
+ * of the tile; anything else runs the bounds-checked form of the same kernel,
+ * which zero-fills out-of-range loads and masks stores ("Pipeline GPU
+ * Kernel", Common Pitfalls: boundary handling with async copies).
+ * Errors: TDG_ERR_NO_DEVICE when the current device is not gfx950 or no
+ * device is present; TDG_ERR_UNSUPPORTED for an explicit configuration that is
+ * not built in or does not fit the device; TDG_ERR_LAUNCH when the launch
+ * itself fails.
+ */
+#ifndef TDGEMM_H
+#define TDGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TDG_OK = 0,
+    TDG_ERR_INVALID_ARG = -1,
+    TDG_ERR_UNSUPPORTED = -2,
+    TDG_ERR_LAUNCH = -3,
+    TDG_ERR_NO_DEVICE = -4
+} tdg_status;
+
+typedef enum {
+    TDG_DTYPE_F16F32 = 0, /* binary16 inputs, FP32 accumulate and output */
+    TDG_DTYPE_I8I32 = 1   /* int8 inputs, INT32 accumulate and output */
+} tdg_dtype;
+
+typedef enum {
+    TDG_VARIANT_AUTO = 0,         /* let tdg_plan choose */
+    TDG_VARIANT_SINGLE = 1,       /* sequential load-barrier-compute-barrier */
+    TDG_VARIANT_REG_PREFETCH = 2, /* global -> registers for t+1 during compute on t */
+    TDG_VARIANT_DIRECT_LDS = 3    /* global -> LDS (LDS-DMA) for t+1 during compute on t */
+} tdg_variant;
+
+/* One kernel configuration.  bk is in elements (64 for FP16, 128 for INT8 at
+ * the default 128-byte K tile); waves is the wavefront count per workgroup
+ * (64 lanes each); lds_stages is 1 or 2. */
+typedef struct {
+    int bm, bn, bk, waves, lds_stages, variant;
+} tdg_config;
+
+/* What the planner computed for a shape and a configuration.
+ *   ratio     -- per-tile compute/load ratio 2*BM*BN*BK / ((BM*BK + BK*BN) *
+ *                sizeof(T)) in operations per byte ("Pipeline GPU Kernel",
+ *                Step 2);
+ *   band      -- 0: ratio < 5, 1: 5 <= ratio <= 20, 2: ratio > 20 (the
+ *                pages' decision thresholds, measured on another GPU);
+ *   lds_bytes -- LDS per workgroup: lds_stages * (BM*BK + BK*BN) * sizeof(T)
+ *                ("Pipeline GPU Kernel", Step 1);
+ *   wg_per_cu -- workgroups resident per compute unit, the minimum of the LDS
+ *                limit (160 KiB per CU), the wave-slot limit and the register
+ *                limit ("Analyze Kernel Bottleneck", Step 3 and Step 6);
+ *   num_tiles -- ceil(K / BK), the K-loop trip count;
+ *   grid      -- workgroups launched, ceil(M/BM) * ceil(N/BN);
+ *   est_regs  -- estimated 32-bit registers per lane for accumulators plus
+ *                register staging;
+ *   guarded   -- 1 when the shape or alignment needs the bounds-checked form. */
+typedef struct {
+    double ratio;
+    int band;
+    size_t lds_bytes;
+    int wg_per_cu;
+    int64_t num_tiles;
+    int64_t grid;
+    int est_regs;
+    int guarded;
+} tdg_plan_info;
+
+/* Sequential (single-buffer) baseline, FP16 -> FP32. */
+int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream);
+/* Sequential (single-buffer) baseline, INT8 -> INT32. */
+int gemm_i8i32(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+               const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+/* Software-pipelined, double-buffered K loop, FP16 -> FP32. */
+int gemm_f16f32_pipelined(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                          const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream);
+/* Software-pipelined, double-buffered K loop, INT8 -> INT32. */
+int gemm_i8i32_pipelined(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                         const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+/* Explicit configuration (tile, waves, LDS stages, variant), for sweeps and
+ * side-by-side comparisons.  cfg == NULL behaves like the _pipelined call.
+ * Fields left 0 in cfg are filled by the planner.  A configuration that is
+ * not built in returns TDG_ERR_UNSUPPORTED. */
+int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream,
+                   const tdg_config *cfg);
+int gemm_i8i32_ex(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                  const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream,
+                  const tdg_config *cfg);
+
+/* Planner.  Chooses the configuration the _pipelined call would run for this
+ * dtype and shape (variant = TDG_VARIANT_AUTO), or, when `out` holds a
+ * partly filled request on entry (any field non-zero), completes that
+ * request.  Writes the result to *out and its figures to *info (either may be
+ * NULL).  Host-only arithmetic: needs no device. */
+int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info);
+
+/* Number of built-in kernel configurations for a dtype, and the i-th one. */
+int tdg_config_count(int dtype);
+int tdg_config_at(int dtype, int index, tdg_config *out);
+
+/* Human-readable name of a status code (static storage). */
+const char *tdg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDGEMM_H */

@@ -1,0 +1,87 @@
+"""Helpers shared by the GPU tests: device transfer and the parity checks.
+
+Expected values come only from the CPU oracle (or from closed forms); nothing
+here computes a product on the GPU except through the library under test.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+F16 = "f16"
+I8 = "i8"
+
+
+def to_device(x: np.ndarray):
+    """Host operand -> device tensor (binary16 bits as torch.float16)."""
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.float16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def gemm(lib, dtype: str, kind: str, A, B, C=None, cfg=None):
+    """Run one library entry point on device tensors; returns C."""
+    fn = {
+        (F16, "single"): lib.gemm_f16f32, (I8, "single"): lib.gemm_i8i32,
+        (F16, "pipelined"): lib.gemm_f16f32_pipelined, (I8, "pipelined"): lib.gemm_i8i32_pipelined,
+    }.get((dtype, kind))
+    if kind == "ex":
+        ex = lib.gemm_f16f32_ex if dtype == F16 else lib.gemm_i8i32_ex
+        return ex(A, B, C, cfg=cfg)
+    return fn(A, B, C)
+
+
+def check_i8(C_gpu, A: np.ndarray, B: np.ndarray):
+    """INT8 -> INT32 must equal the oracle's int64 result bit for bit."""
+    ref = oracle.gemm_i8(A, B)
+    got = C_gpu.cpu().numpy().astype(np.int64)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, "%d mismatches, first at %s: got %d want %d" % (
+        len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+def check_f16(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False):
+    """FP16 -> FP32 within |err| <= 1e-4 * sum_k |a_ik b_kj| per element
+    (exactly equal when `exact`)."""
+    ref, S = oracle.gemm_f16(A, B)
+    got = C_gpu.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    tol = 0.0 if exact else 1e-4
+    bad = np.argwhere(err > tol * S)
+    assert bad.size == 0, "%d elements out of tolerance, first at %s: got %r want %r (S=%r)" % (
+        len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])], S[tuple(bad[0])])
+
+
+def sample_indices(M: int, N: int, count: int, seed: int, tile_m: int = 256, tile_n: int = 256):
+    """Random (row, col) pairs plus the corners and tile-boundary elements."""
+    rng = np.random.default_rng(seed)
+    rows = list(rng.integers(0, M, count))
+    cols = list(rng.integers(0, N, count))
+    edges_m = sorted({0, M - 1} | {min(M - 1, t) for t in range(tile_m - 1, M, tile_m)} |
+                     {min(M - 1, t) for t in range(0, M, tile_m)})
+    edges_n = sorted({0, N - 1} | {min(N - 1, t) for t in range(tile_n - 1, N, tile_n)} |
+                     {min(N - 1, t) for t in range(0, N, tile_n)})
+    for i in edges_m[:64]:
+        for j in edges_n[:64]:
+            rows.append(i)
+            cols.append(j)
+    return np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64)
+
+
+def check_sampled(C_gpu, dtype: str, A: np.ndarray, B: np.ndarray, rows, cols):
+    got_full = C_gpu.cpu().numpy()
+    got = got_full[rows, cols]
+    if dtype == I8:
+        ref = oracle.gemm_i8_at(A, B, rows, cols)
+        bad = np.nonzero(got.astype(np.int64) != ref)[0]
+        assert bad.size == 0, "%d sampled mismatches, first (%d,%d): got %d want %d" % (
+            bad.size, rows[bad[0]], cols[bad[0]], got[bad[0]], ref[bad[0]])
+    else:
+        ref, S = oracle.gemm_f16_at(A, B, rows, cols)
+        err = np.abs(got.astype(np.float64) - ref)
+        bad = np.nonzero(err > 1e-4 * S)[0]
+        assert bad.size == 0, "%d sampled out of tolerance, first (%d,%d): got %r want %r" % (
+            bad.size, rows[bad[0]], cols[bad[0]], got[bad[0]], ref[bad[0]])
+    return got_full

@@ -1,0 +1,325 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+INT8 -> INT32 must match bit for bit; FP16 -> FP32 must satisfy
+|C_gpu - C| <= 1e-4 * sum_k |a_ik b_kj| per element, and integer-valued FP16
+inputs (every partial sum exact in FP32) must match exactly.  Pipelining only
+reorders loads ("Pipeline GPU Kernel", Step 5), so every variant of one tile
+configuration must produce bitwise-identical output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic_inputs as si
+from gpu_util import F16, I8, check_f16, check_i8, check_sampled, gemm, sample_indices, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import tiled_dense_gemm_loop_amd as t
+    t.load_library()
+    return t
+
+
+def _operands(dtype, M, N, K, seed, dist="normal"):
+    if dtype == I8:
+        return si.i8_uniform(M, K, seed), si.i8_uniform(K, N, seed + 1)
+    if dist == "int":
+        return si.f16_integers(M, K, seed), si.f16_integers(K, N, seed + 1)
+    return si.f16_normal(M, K, seed), si.f16_normal(K, N, seed + 1)
+
+
+def _check(dtype, C, A, B, exact=False):
+    if dtype == I8:
+        check_i8(C, A, B)
+    else:
+        check_f16(C, A, B, exact=exact)
+
+
+def _variants(lib, dtype, tile):
+    """All four loop forms at one tile shape: (name, cfg)."""
+    base = {"bm": tile["bm"], "bn": tile["bn"], "bk": tile["bk"], "waves": tile["waves"]}
+    return [
+        ("single", dict(base, variant=lib.TDG_VARIANT_SINGLE, lds_stages=1)),
+        ("reg_s1", dict(base, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=1)),
+        ("reg_s2", dict(base, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)),
+        ("direct", dict(base, variant=lib.TDG_VARIANT_DIRECT_LDS, lds_stages=2)),
+    ]
+
+
+def _tiles(dtype_code):
+    import tiled_dense_gemm_loop_amd as t
+    seen, out = set(), []
+    for i in range(t.tdg_config_count(dtype_code)):
+        c = t.tdg_config_at(dtype_code, i)
+        key = (c["bm"], c["bn"], c["bk"], c["waves"])
+        if key not in seen:
+            seen.add(key)
+            out.append(dict(zip(("bm", "bn", "bk", "waves"), key)))
+    return out
+
+
+def _all_tiles():
+    try:
+        return [(F16, c) for c in _tiles(0)] + [(I8, c) for c in _tiles(1)]
+    except ImportError:
+        return []
+
+
+# --- the small workloads, whole-matrix parity ---------------------------------------
+
+def test_int8_256_every_entry_point(lib):
+    wl = si.WORKLOADS["int8_256"]
+    A, B = wl.operands()
+    dA, dB = to_device(A), to_device(B)
+    outs = []
+    for kind in ("single", "pipelined"):
+        C = gemm(lib, I8, kind, dA, dB)
+        check_i8(C, A, B)
+        outs.append(C)
+    tile, _ = lib.tdg_plan(lib.TDG_DTYPE_I8I32, wl.M, wl.N, wl.K)
+    for name, cfg in _variants(lib, I8, tile):
+        C = gemm(lib, I8, "ex", dA, dB, cfg=cfg)
+        check_i8(C, A, B)
+
+
+def test_fp16_1024_single_vs_pipelined(lib):
+    import torch
+    wl = si.WORKLOADS["fp16_1024"]
+    A, B = wl.operands()
+    dA, dB = to_device(A), to_device(B)
+    C1 = gemm(lib, F16, "single", dA, dB)
+    C2 = gemm(lib, F16, "pipelined", dA, dB)
+    check_f16(C1, A, B)
+    check_f16(C2, A, B)
+    assert torch.equal(C1, C2), "single and pipelined differ at the same tile"
+
+
+# --- every built tile shape x every loop form ------------------------------------------
+
+@pytest.mark.parametrize("dtype,tile", _all_tiles(),
+                         ids=lambda v: v if isinstance(v, str) else
+                         "%dx%dx%d_w%d" % (v["bm"], v["bn"], v["bk"], v["waves"]))
+def test_tile_shape_all_variants(lib, dtype, tile):
+    import torch
+    M, N, K = 2 * tile["bm"], 2 * tile["bn"], 3 * tile["bk"]
+    A, B = _operands(dtype, M, N, K, seed=M + N + K)
+    dA, dB = to_device(A), to_device(B)
+    ref_out = None
+    for name, cfg in _variants(lib, dtype, tile):
+        C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+        _check(dtype, C, A, B)
+        if ref_out is None:
+            ref_out = C
+        else:
+            assert torch.equal(ref_out, C), "variant %s differs from single" % name
+
+
+# --- ragged, tiny and degenerate shapes (bounds-checked path) ---------------------------
+
+RAGGED = [(1, 1, 1), (5, 7, 3), (64, 64, 1), (33, 65, 17), (300, 290, 333), (257, 129, 65),
+          (130, 260, 200), (1000, 3, 70), (3, 1000, 129), (64, 64, 63)]
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_ragged_shapes(lib, dtype, M, N, K):
+    A, B = _operands(dtype, M, N, K, seed=7 * M + N + K)
+    dA, dB = to_device(A), to_device(B)
+    for kind in ("single", "pipelined"):
+        _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_ragged_every_tile(lib, dtype):
+    M, N, K = 301, 283, 259
+    A, B = _operands(dtype, M, N, K, seed=99)
+    dA, dB = to_device(A), to_device(B)
+    for tile in (_tiles(0) if dtype == F16 else _tiles(1)):
+        for name, cfg in _variants(lib, dtype, tile):
+            _check(dtype, gemm(lib, dtype, "ex", dA, dB, cfg=cfg), A, B)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_k_zero_writes_zeros(lib, dtype):
+    import torch
+    M, N = 300, 260
+    A = np.zeros((M, 0), dtype=np.uint16 if dtype == F16 else np.int8)
+    B = np.zeros((0, N), dtype=A.dtype)
+    out_t = torch.float32 if dtype == F16 else torch.int32
+    for kind in ("single", "pipelined"):
+        C = torch.full((M, N), 7, dtype=out_t, device="cuda")
+        gemm(lib, dtype, kind, to_device(A), to_device(B), C)
+        assert torch.count_nonzero(C).item() == 0
+
+
+def test_empty_outputs_are_noops(lib):
+    import torch
+    for (M, N, K) in [(0, 5, 7), (5, 0, 7), (0, 0, 0)]:
+        A = torch.zeros((M, K), dtype=torch.int8, device="cuda")
+        B = torch.zeros((K, N), dtype=torch.int8, device="cuda")
+        C = gemm(lib, I8, "pipelined", A, B)
+        assert C.shape == (M, N)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_strided_and_misaligned_operands(lib, dtype):
+    """Leading dimensions wider than the matrix, and base pointers that are
+    not 16-byte aligned: the fast path must be skipped, results unchanged."""
+    M, N, K = 512, 256, 320
+    bigA, bigB = _operands(dtype, M + 3, N + 40, K + 40, seed=5)
+    for (ao, bo) in [(0, 0), (1, 3)]:
+        A = bigA[1:1 + M, ao:ao + K]
+        B = bigB[2:2 + K, bo:bo + N]
+        dBigA, dBigB = to_device(bigA), to_device(bigB)
+        dA = dBigA[1:1 + M, ao:ao + K]
+        dB = dBigB[2:2 + K, bo:bo + N]
+        for kind in ("single", "pipelined"):
+            _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
+
+
+def test_output_leading_dimension(lib):
+    import torch
+    M, N, K = 256, 256, 192
+    A, B = _operands(I8, M, N, K, seed=11)
+    big = torch.full((M, N + 64), -5, dtype=torch.int32, device="cuda")
+    C = big[:, 32:32 + N]
+    gemm(lib, I8, "pipelined", to_device(A), to_device(B), C)
+    check_i8(C, A, B)
+    assert torch.all(big[:, :32] == -5) and torch.all(big[:, 32 + N:] == -5)
+
+
+# --- pins on the GPU ------------------------------------------------------------------------
+
+def test_integer_valued_fp16_is_exact(lib):
+    """Integers in [-8, 8]: every partial sum is an integer below 2^24, so any
+    FP32 summation order is exact and the result must equal the oracle."""
+    for (M, N, K) in [(1024, 1024, 1024), (512, 768, 640), (300, 290, 333)]:
+        A, B = _operands(F16, M, N, K, seed=M + 2 * N, dist="int")
+        dA, dB = to_device(A), to_device(B)
+        for kind in ("single", "pipelined"):
+            check_f16(gemm(lib, F16, kind, dA, dB), A, B, exact=True)
+
+
+def test_exhaustive_int8_product_table(lib):
+    vals = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+    A = vals.reshape(256, 1).copy()
+    B = vals[::-1].reshape(1, 256).copy()
+    for kind in ("single", "pipelined"):
+        check_i8(gemm(lib, I8, kind, to_device(A), to_device(B)), A, B)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_identity(lib, dtype):
+    n = 512
+    A, _ = _operands(dtype, n, n, n, seed=21)
+    if dtype == F16:
+        one = np.float16(1.0).view(np.uint16)
+        I = np.where(np.eye(n, dtype=bool), one, np.uint16(0)).astype(np.uint16)
+        expect = A.view(np.float16).astype(np.float32)
+    else:
+        I = np.eye(n, dtype=np.int8)
+        expect = A.astype(np.int32)
+    dA, dI = to_device(A), to_device(I)
+    for kind in ("single", "pipelined"):
+        assert np.array_equal(gemm(lib, dtype, kind, dA, dI).cpu().numpy(), expect)
+        assert np.array_equal(gemm(lib, dtype, kind, dI, dA).cpu().numpy(),
+                              expect if dtype == I8 else expect)
+
+
+def test_rank1_extremes_int8(lib):
+    """A[i][k] = u_i, B[k][j] = v_j: C = K u_i v_j, up to 4096 * 16384."""
+    M, N, K = 512, 512, 4096
+    u = np.resize(np.array([-128, 127, 1, -1, 0, 64, -64, 5], dtype=np.int8), M)
+    v = np.resize(np.array([127, -128, -1, 1, 3, 0, 100, -7], dtype=np.int8), N)
+    A = np.repeat(u.reshape(M, 1), K, axis=1)
+    B = np.repeat(v.reshape(1, N), K, axis=0)
+    expect = K * np.outer(u.astype(np.int64), v.astype(np.int64))
+    for kind in ("single", "pipelined"):
+        got = gemm(lib, I8, kind, to_device(A), to_device(B)).cpu().numpy()
+        assert np.array_equal(got.astype(np.int64), expect)
+
+
+def test_all_ones_detects_a_dropped_tile(lib):
+    """All-ones operands give C = K everywhere; a lost K tile would give K - BK."""
+    import torch
+    M, N, K = 512, 512, 1024
+    for dtype in (F16, I8):
+        if dtype == F16:
+            A = np.full((M, K), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+            B = np.full((K, N), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+        else:
+            A = np.ones((M, K), dtype=np.int8)
+            B = np.ones((K, N), dtype=np.int8)
+        for kind in ("single", "pipelined"):
+            C = gemm(lib, dtype, kind, to_device(A), to_device(B))
+            assert torch.all(C == K)
+
+
+def test_k_split_additivity(lib):
+    """C(A, B) == C(A[:, :k1], B[:k1]) + C(A[:, k1:], B[k1:]) exactly for INT8,
+    with the halves passed as pointer offsets into the same matrices."""
+    import torch
+    M, N, K = 512, 512, 1024
+    A, B = _operands(I8, M, N, K, seed=31)
+    dA, dB = to_device(A), to_device(B)
+    full = gemm(lib, I8, "pipelined", dA, dB)
+    for k1 in (128, 384, 512):
+        part = gemm(lib, I8, "pipelined", dA[:, :k1], dB[:k1]) + \
+            gemm(lib, I8, "pipelined", dA[:, k1:], dB[k1:])
+        assert torch.equal(full, part)
+
+
+def test_repeat_runs_are_bitwise_identical(lib):
+    import torch
+    wl = si.WORKLOADS["fp16_1024"]
+    A, B = wl.operands()
+    dA, dB = to_device(A), to_device(B)
+    first = gemm(lib, F16, "pipelined", dA, dB)
+    for _ in range(10):
+        assert torch.equal(first, gemm(lib, F16, "pipelined", dA, dB))
+
+
+def test_invalid_arguments_are_rejected(lib):
+    import torch
+    A = torch.zeros((64, 64), dtype=torch.int8, device="cuda")
+    B = torch.zeros((64, 64), dtype=torch.int8, device="cuda")
+    buf = torch.zeros((64 * 64,), dtype=torch.int32, device="cuda")
+    p = buf.data_ptr()
+    # C overlapping A
+    assert lib.call_raw("gemm_i8i32_pipelined", 16, 16, 16, p, 16, B.data_ptr(), 64, p, 16) == \
+        lib.TDG_ERR_INVALID_ARG
+    # lda too small
+    assert lib.call_raw("gemm_i8i32", 64, 64, 64, A.data_ptr(), 32, B.data_ptr(), 64, p, 64) == \
+        lib.TDG_ERR_INVALID_ARG
+    # explicit tile that is not built
+    cfg = lib.TdgConfig(bm=96, bn=96, bk=0, waves=0, lds_stages=0, variant=0)
+    assert lib.call_raw("gemm_i8i32_ex", 64, 64, 64, A.data_ptr(), 64, B.data_ptr(), 64, p, 64,
+                        0, cfg) == lib.TDG_ERR_UNSUPPORTED
+
+
+# --- the full-size workloads, in the configuration the benchmark times ---------------------
+
+@pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny"])
+def test_full_size_sampled(lib, name):
+    import torch
+    wl = si.WORKLOADS[name]
+    A, B = wl.operands()
+    dA, dB = to_device(A), to_device(B)
+    dtype = I8 if wl.dtype == "i8" else F16
+    rows, cols = sample_indices(wl.M, wl.N, 3000, seed=wl.seed_a, tile_n=min(256, wl.N))
+    C_pipe = gemm(lib, dtype, "pipelined", dA, dB)
+    check_sampled(C_pipe, dtype, A, B, rows, cols)
+    C_single = gemm(lib, dtype, "single", dA, dB)
+    check_sampled(C_single, dtype, A, B, rows, cols)
+    assert torch.equal(C_pipe, C_single)
+    tile, _ = lib.tdg_plan(0 if dtype == F16 else 1, wl.M, wl.N, wl.K)
+    for vname, cfg in _variants(lib, dtype, tile):
+        assert torch.equal(C_pipe, gemm(lib, dtype, "ex", dA, dB, cfg=cfg)), vname
+    del C_pipe, C_single, dA, dB
+    torch.cuda.empty_cache()

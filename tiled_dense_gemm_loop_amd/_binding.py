@@ -1,0 +1,229 @@
+"""ctypes binding of libtdgemm.so (the C ABI in include/tdgemm.h).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  Tensors give device pointers, shapes and row strides; the
+stream is torch's current stream on the operands' device.  There is no CPU
+fallback -- a missing library or device raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtdgemm.so")
+
+TDG_OK = 0
+TDG_ERR_INVALID_ARG = -1
+TDG_ERR_UNSUPPORTED = -2
+TDG_ERR_LAUNCH = -3
+TDG_ERR_NO_DEVICE = -4
+
+TDG_DTYPE_F16F32 = 0
+TDG_DTYPE_I8I32 = 1
+
+TDG_VARIANT_AUTO = 0
+TDG_VARIANT_SINGLE = 1
+TDG_VARIANT_REG_PREFETCH = 2
+TDG_VARIANT_DIRECT_LDS = 3
+
+VARIANT_NAMES = {0: "auto", 1: "single", 2: "reg_prefetch", 3: "direct_lds"}
+
+# Every symbol include/tdgemm.h declares.
+EXPORTED = (
+    "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
+    "gemm_f16f32_ex", "gemm_i8i32_ex", "tdg_plan", "tdg_config_count", "tdg_config_at",
+    "tdg_status_string",
+)
+
+
+class TdgConfig(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
+                ("waves", ctypes.c_int), ("lds_stages", ctypes.c_int), ("variant", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class TdgPlanInfo(ctypes.Structure):
+    _fields_ = [("ratio", ctypes.c_double), ("band", ctypes.c_int), ("lds_bytes", ctypes.c_size_t),
+                ("wg_per_cu", ctypes.c_int), ("num_tiles", ctypes.c_int64),
+                ("grid", ctypes.c_int64), ("est_regs", ctypes.c_int), ("guarded", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class TdgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtdgemm.so (built by tiled_dense_gemm_loop_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch ships its own HIP runtime under the same soname
+    # (libamdhip64.so.7).  Loading torch first makes this library bind to
+    # that one runtime, so device pointers and torch's hipStream_t handles
+    # mean the same thing on both sides; loading the library first would put
+    # a second HIP runtime into the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise ImportError("libtdgemm.so is not built (%s); run __graft_entry__.build() or "
+                          "python tiled_dense_gemm_loop_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    for name in ("gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined"):
+        fn = getattr(lib, name)
+        fn.argtypes = gemm_args
+        fn.restype = c_int
+    for name in ("gemm_f16f32_ex", "gemm_i8i32_ex"):
+        fn = getattr(lib, name)
+        fn.argtypes = gemm_args + [ctypes.POINTER(TdgConfig)]
+        fn.restype = c_int
+    lib.tdg_plan.argtypes = [c_int, i64, i64, i64, ctypes.POINTER(TdgConfig),
+                             ctypes.POINTER(TdgPlanInfo)]
+    lib.tdg_plan.restype = c_int
+    lib.tdg_config_count.argtypes = [c_int]
+    lib.tdg_config_count.restype = c_int
+    lib.tdg_config_at.argtypes = [c_int, c_int, ctypes.POINTER(TdgConfig)]
+    lib.tdg_config_at.restype = c_int
+    lib.tdg_status_string.argtypes = [c_int]
+    lib.tdg_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tdg_status_string(status).decode()
+
+
+# ------------------------------------------------------------------ raw calls
+
+def call_raw(name: str, M, N, K, a_ptr, lda, b_ptr, ldb, c_ptr, ldc, stream=0, cfg=None) -> int:
+    """Call a GEMM entry point with raw device pointers; returns the status."""
+    fn = getattr(load_library(), name)
+    args = [M, N, K, a_ptr, lda, b_ptr, ldb, c_ptr, ldc, stream]
+    if name.endswith("_ex"):
+        args.append(ctypes.byref(cfg) if cfg is not None else None)
+    return fn(*args)
+
+
+# -------------------------------------------------------------- torch tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _matrix(t, dtypes, what):
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (what, tuple(t.shape)))
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s; expected one of %s" % (what, t.dtype, dtypes))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    rows, cols = t.shape
+    if t.numel() == 0:
+        return rows, cols, t.data_ptr(), max(cols, 1)
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("%s: elements within a row must be contiguous" % what)
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return rows, cols, t.data_ptr(), max(ld, 1)
+
+
+def _gemm(name, A, B, C, cfg, f16):
+    torch = _torch()
+    in_types = (torch.float16, torch.int16) if f16 else (torch.int8,)
+    M, K, pa, lda = _matrix(A, in_types, "A")
+    K2, N, pb, ldb = _matrix(B, in_types, "B")
+    if K != K2:
+        raise ValueError("inner dimensions differ: A is %dx%d, B is %dx%d" % (M, K, K2, N))
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    out_type = torch.float32 if f16 else torch.int32
+    if C is None:
+        C = torch.empty((M, N), dtype=out_type, device=A.device)
+    Mc, Nc, pc, ldc = _matrix(C, (out_type,), "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError("C has shape %s, expected %s" % ((Mc, Nc), (M, N)))
+    with torch.cuda.device(A.device):
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+        rc = call_raw(name, M, N, K, pa, lda, pb, ldb, pc, ldc, stream, cfg)
+    if rc != TDG_OK:
+        raise TdgError(rc, name)
+    return C
+
+
+def _cfg(cfg):
+    if cfg is None or isinstance(cfg, TdgConfig):
+        return cfg
+    c = TdgConfig()
+    for k, v in dict(cfg).items():
+        setattr(c, k, int(v))
+    return c
+
+
+def gemm_f16f32(A, B, C=None):
+    """Sequential single-buffer baseline: C (float32) = A . B (float16)."""
+    return _gemm("gemm_f16f32", A, B, C, None, True)
+
+
+def gemm_i8i32(A, B, C=None):
+    """Sequential single-buffer baseline: C (int32) = A . B (int8)."""
+    return _gemm("gemm_i8i32", A, B, C, None, False)
+
+
+def gemm_f16f32_pipelined(A, B, C=None):
+    """Software-pipelined double-buffered K loop, FP16 -> FP32."""
+    return _gemm("gemm_f16f32_pipelined", A, B, C, None, True)
+
+
+def gemm_i8i32_pipelined(A, B, C=None):
+    """Software-pipelined double-buffered K loop, INT8 -> INT32."""
+    return _gemm("gemm_i8i32_pipelined", A, B, C, None, False)
+
+
+def gemm_f16f32_ex(A, B, C=None, cfg=None):
+    """Explicit configuration (dict or TdgConfig; zero fields are planned)."""
+    return _gemm("gemm_f16f32_ex", A, B, C, _cfg(cfg), True)
+
+
+def gemm_i8i32_ex(A, B, C=None, cfg=None):
+    return _gemm("gemm_i8i32_ex", A, B, C, _cfg(cfg), False)
+
+
+def tdg_plan(dtype: int, M: int, N: int, K: int, cfg=None):
+    """(config dict, plan-info dict) the planner picks for this shape."""
+    c = _cfg(cfg) or TdgConfig()
+    info = TdgPlanInfo()
+    rc = load_library().tdg_plan(dtype, M, N, K, ctypes.byref(c), ctypes.byref(info))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_plan")
+    return c.as_dict(), info.as_dict()
+
+
+def tdg_config_count(dtype: int) -> int:
+    return load_library().tdg_config_count(dtype)
+
+
+def tdg_config_at(dtype: int, index: int) -> dict:
+    c = TdgConfig()
+    rc = load_library().tdg_config_at(dtype, index, ctypes.byref(c))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_config_at")
+    return c.as_dict()
+
+
+def tdg_status_string(status: int) -> str:
+    return status_string(status)

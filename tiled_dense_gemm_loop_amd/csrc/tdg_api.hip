@@ -1,0 +1,428 @@
+// tdg_api.hip -- host side of the C ABI declared in include/tdgemm.h:
+// argument validation, the tile/variant planner and kernel dispatch.
+//
+// Validation and planning are plain host arithmetic and run before any HIP
+// call, so a bad argument never reaches the device.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "tdg_internal.h"
+#include "tdg_kernels.hpp"
+#include "tdgemm.h"
+
+namespace tdg {
+
+// Both dtype tables, concatenated once.
+const KernelEntry *kernel_table(int *count) {
+    static KernelEntry all[256];
+    static int n = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int nf = 0, ni = 0;
+        const KernelEntry *f = kernel_table_f16(&nf);
+        const KernelEntry *i = kernel_table_i8(&ni);
+        for (int k = 0; k < nf && n < 256; k++) all[n++] = f[k];
+        for (int k = 0; k < ni && n < 256; k++) all[n++] = i[k];
+    });
+    *count = n;
+    return all;
+}
+
+}  // namespace tdg
+
+namespace {
+
+using tdg::KernelEntry;
+
+constexpr int kNumCU = 256;               // MI355X compute units
+constexpr int kLdsPerCU = 160 * 1024;     // gfx950 LDS per CU
+constexpr int kWaveSlotsPerCU = 4 * 8;    // 4 SIMDs x 8 wave slots
+constexpr int kRegsPerLanePerSIMD = 512;  // unified VGPR + AGPR file
+
+int elem_size(int dtype) { return dtype == TDG_DTYPE_F16F32 ? 2 : 1; }
+
+// ---------------------------------------------------------------- validation
+
+bool ranges_overlap(uintptr_t a0, uint64_t alen, uintptr_t b0, uint64_t blen) {
+    if (alen == 0 || blen == 0) return false;
+    return a0 < b0 + blen && b0 < a0 + alen;
+}
+
+// Bytes spanned by a rows x cols row-major matrix with leading dimension ld.
+uint64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
+    if (rows == 0 || cols == 0) return 0;
+    return (uint64_t)((rows - 1) * ld + cols) * (uint64_t)es;
+}
+
+int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+             int64_t ldb, const void *C, int64_t ldc) {
+    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return TDG_ERR_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return TDG_ERR_INVALID_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return TDG_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && !A) return TDG_ERR_INVALID_ARG;
+    if (K > 0 && N > 0 && !B) return TDG_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && !C) return TDG_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    const uint64_t cspan = span_bytes(M, N, ldc, 4);
+    if (ranges_overlap((uintptr_t)C, cspan, (uintptr_t)A, span_bytes(M, K, lda, es)) ||
+        ranges_overlap((uintptr_t)C, cspan, (uintptr_t)B, span_bytes(K, N, ldb, es)))
+        return TDG_ERR_INVALID_ARG;
+    return TDG_OK;
+}
+
+// ------------------------------------------------------------------ planner
+
+int cfg_waves(const KernelEntry &e) { return e.wm * e.wn; }
+int cfg_bk(const KernelEntry &e) { return e.bkb / elem_size(e.dtype); }
+
+bool same_tile(const KernelEntry &a, const KernelEntry &b) {
+    return a.dtype == b.dtype && a.bm == b.bm && a.bn == b.bn && a.bkb == b.bkb && a.wm == b.wm &&
+           a.wn == b.wn;
+}
+
+// Does this request (zeros = "any") match the entry's tile shape?
+bool tile_matches(const tdg_config &req, const KernelEntry &e) {
+    return (req.bm == 0 || req.bm == e.bm) && (req.bn == 0 || req.bn == e.bn) &&
+           (req.bk == 0 || req.bk == cfg_bk(e)) && (req.waves == 0 || req.waves == cfg_waves(e));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Whether the unguarded fast path may run: whole tiles, 16-byte aligned
+// operands and rows, and per-tile offsets inside 32 bits.
+bool fast_ok(const KernelEntry &e, int64_t M, int64_t N, int64_t K, bool vec_ok) {
+    const int bk = cfg_bk(e);
+    if (K == 0 || M % e.bm || N % e.bn || K % bk) return false;
+    return vec_ok;
+}
+
+bool aligned_operands(int dtype, const void *A, int64_t lda, const void *B, int64_t ldb) {
+    const int es = elem_size(dtype);
+    return ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((lda * es) % 16 == 0) &&
+           ((ldb * es) % 16 == 0);
+}
+
+// Per-lane 32-bit offsets cover up to 64 rows of A or B plus one row of
+// bytes; the planner refuses leading dimensions that would overflow them.
+bool offsets_fit(int dtype, int64_t lda, int64_t ldb) {
+    const int64_t es = elem_size(dtype);
+    const int64_t lim = (int64_t)1 << 31;
+    return 64 * lda * es + 256 < lim && 64 * ldb * es + 256 < lim;
+}
+
+// Estimated 32-bit registers per lane: accumulators plus staging.
+int est_regs(const KernelEntry &e, int variant) {
+    const int waves = cfg_waves(e);
+    const int acc = e.bm * e.bn / (waves * 64);
+    const int stage_bytes = (e.bm + e.bn) * e.bkb;  // one K tile of A and B
+    const int staging = variant == TDG_VARIANT_DIRECT_LDS ? 0 : stage_bytes / (waves * 64) / 4;
+    const int frags = 4 * (e.bm / e.wm / 32 + e.bn / e.wn / 32) * 2;
+    return acc + staging + frags + 24;
+}
+
+void fill_info(const KernelEntry &e, int variant, int stages, int64_t M, int64_t N, int64_t K,
+               bool guarded, tdg_plan_info *info) {
+    if (!info) return;
+    const int es = elem_size(e.dtype);
+    const int bk = cfg_bk(e);
+    // "Pipeline GPU Kernel", Step 2: operations per byte loaded per tile.
+    const double flops = 2.0 * e.bm * e.bn * bk;
+    const double bytes = (double)(e.bm * bk + bk * e.bn) * es;
+    info->ratio = flops / bytes;
+    info->band = info->ratio < 5.0 ? 0 : (info->ratio <= 20.0 ? 1 : 2);
+    // "Pipeline GPU Kernel", Step 1: one buffer = (BM*BK + BK*BN)*sizeof(T).
+    info->lds_bytes = (size_t)stages * (size_t)(e.bm * bk + bk * e.bn) * (size_t)es;
+    const int waves = cfg_waves(e);
+    int by_lds = info->lds_bytes ? (int)(kLdsPerCU / info->lds_bytes) : 64;
+    int by_waves = kWaveSlotsPerCU / waves;
+    const int regs = est_regs(e, variant);
+    int waves_per_simd = kRegsPerLanePerSIMD / (regs < 1 ? 1 : regs);
+    if (waves_per_simd > 8) waves_per_simd = 8;
+    int by_regs = waves_per_simd * 4 / waves;
+    int wg = by_lds < by_waves ? by_lds : by_waves;
+    wg = wg < by_regs ? wg : by_regs;
+    info->wg_per_cu = wg;
+    info->num_tiles = ceil_div(K, bk);
+    info->grid = ceil_div(M, e.bm) * ceil_div(N, e.bn);
+    info->est_regs = regs;
+    info->guarded = guarded ? 1 : 0;
+}
+
+// Measured choice of tile shape: the largest tile that still gives every
+// compute unit a workgroup; when no tile does, the one giving the most
+// workgroups.  Skinny products (N <= 64) use the 64-column tiles.
+const KernelEntry *choose_tile(int dtype, int64_t M, int64_t N, int64_t K, const tdg_config &req) {
+    int count = 0;
+    const KernelEntry *table = tdg::kernel_table(&count);
+    const KernelEntry *best = nullptr;
+    int64_t best_area = -1, best_grid = -1;
+    bool best_fills = false;
+    (void)K;
+    for (int i = 0; i < count; i++) {
+        const KernelEntry &e = table[i];
+        if (e.dtype != dtype || e.guard || e.variant != TDG_VARIANT_SINGLE) continue;
+        if (!tile_matches(req, e)) continue;
+        // auto selection only considers the default K tile and 4 waves
+        if (req.bk == 0 && e.bkb != 128) continue;
+        if (req.waves == 0 && cfg_waves(e) != 4) continue;
+        if (req.bn == 0 && N <= 64 && e.bn != 64) continue;
+        const int64_t grid = ceil_div(M, e.bm) * ceil_div(N, e.bn);
+        const int64_t area = (int64_t)e.bm * e.bn;
+        const bool fills = grid >= kNumCU;
+        bool better;
+        if (!best) better = true;
+        else if (fills != best_fills) better = fills;
+        else if (fills) better = area > best_area;
+        else better = grid > best_grid || (grid == best_grid && area > best_area);
+        if (better) {
+            best = &e;
+            best_area = area;
+            best_grid = grid;
+            best_fills = fills;
+        }
+    }
+    return best;
+}
+
+const KernelEntry *find_entry(const KernelEntry &tile, int stages, int variant, bool guard) {
+    int count = 0;
+    const KernelEntry *table = tdg::kernel_table(&count);
+    for (int i = 0; i < count; i++) {
+        const KernelEntry &e = table[i];
+        if (same_tile(e, tile) && e.stages == stages && e.variant == variant && e.guard == guard)
+            return &e;
+    }
+    return nullptr;
+}
+
+struct Resolved {
+    const KernelEntry *entry;  // kernel to launch
+    int variant, stages;
+    bool guarded;
+};
+
+// Complete a (possibly partial) request into a runnable kernel.
+int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+            int64_t ldb, const tdg_config &req_in, bool pipelined_default, Resolved *out,
+            tdg_config *cfg_out, tdg_plan_info *info) {
+    tdg_config req = req_in;
+    if (req.variant < 0 || req.variant > TDG_VARIANT_DIRECT_LDS) return TDG_ERR_INVALID_ARG;
+    if (req.lds_stages < 0 || req.lds_stages > 2) return TDG_ERR_UNSUPPORTED;
+    const KernelEntry *tile = choose_tile(dtype, M, N, K, req);
+    if (!tile) return TDG_ERR_UNSUPPORTED;
+    const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
+    const bool fast = fast_ok(*tile, M, N, K, vec_ok);
+
+    int variant = req.variant;
+    if (variant == TDG_VARIANT_AUTO)
+        variant = pipelined_default ? (fast ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
+                                    : TDG_VARIANT_SINGLE;
+    int stages = req.lds_stages;
+    if (stages == 0) stages = variant == TDG_VARIANT_SINGLE ? 1 : 2;
+    if (variant == TDG_VARIANT_SINGLE && stages != 1) return TDG_ERR_UNSUPPORTED;
+    if (variant == TDG_VARIANT_DIRECT_LDS && stages != 2) return TDG_ERR_UNSUPPORTED;
+
+    bool guard = !fast;
+    const KernelEntry *e = nullptr;
+    if (!guard) {
+        e = find_entry(*tile, stages, variant, false);
+    } else if (variant == TDG_VARIANT_DIRECT_LDS) {
+        // The DMA needs valid, aligned sources for every 16-byte chunk; ragged
+        // or misaligned operands run the bounds-checked register-prefetch
+        // loop instead ("Pipeline GPU Kernel", Common Pitfalls).
+        variant = TDG_VARIANT_REG_PREFETCH;
+        e = find_entry(*tile, 2, variant, true);
+        stages = 2;
+    } else if (variant == TDG_VARIANT_REG_PREFETCH && stages == 1) {
+        e = find_entry(*tile, 2, variant, true);
+        stages = 2;
+    } else {
+        e = find_entry(*tile, stages, variant, true);
+    }
+    if (!e) return TDG_ERR_UNSUPPORTED;
+    if (e->lds_bytes > kLdsPerCU) return TDG_ERR_UNSUPPORTED;
+    if (!offsets_fit(dtype, lda, ldb)) return TDG_ERR_UNSUPPORTED;
+
+    if (out) {
+        out->entry = e;
+        out->variant = variant;
+        out->stages = stages;
+        out->guarded = guard;
+    }
+    if (cfg_out) {
+        cfg_out->bm = e->bm;
+        cfg_out->bn = e->bn;
+        cfg_out->bk = cfg_bk(*e);
+        cfg_out->waves = cfg_waves(*e);
+        cfg_out->lds_stages = stages;
+        cfg_out->variant = variant;
+    }
+    fill_info(*e, variant, stages, M, N, K, guard, info);
+    return TDG_OK;
+}
+
+// ------------------------------------------------------------------- device
+
+std::mutex g_dev_mutex;
+signed char g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int device_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TDG_ERR_NO_DEVICE;
+    if (dev < 0 || dev >= 64) return TDG_ERR_NO_DEVICE;
+    {
+        std::lock_guard<std::mutex> lock(g_dev_mutex);
+        if (g_dev_ok[dev] == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TDG_ERR_NO_DEVICE;
+            g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        }
+        if (g_dev_ok[dev] != 1) return TDG_ERR_NO_DEVICE;
+    }
+    return TDG_OK;
+}
+
+int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+        int64_t ldb, void *C, int64_t ldc, void *stream, const tdg_config *cfg,
+        bool pipelined_default) {
+    int rc = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+    if (rc != TDG_OK) return rc;
+    if (M == 0 || N == 0) return TDG_OK;
+    tdg_config req;
+    memset(&req, 0, sizeof(req));
+    if (cfg) req = *cfg;
+    Resolved r;
+    rc = resolve(dtype, M, N, K, A, lda, B, ldb, req, pipelined_default, &r, nullptr, nullptr);
+    if (rc != TDG_OK) return rc;
+    rc = device_check();
+    if (rc != TDG_OK) return rc;
+
+    const KernelEntry &e = *r.entry;
+    tdg::GemmArgs args;
+    args.A = (const unsigned char *)A;
+    args.B = (const unsigned char *)B;
+    args.C = (unsigned char *)C;
+    args.lda = lda;
+    args.ldb = ldb;
+    args.ldc = ldc;
+    args.M = (int)M;
+    args.N = (int)N;
+    args.K = (int)K;
+    args.tiles_m = (int)ceil_div(M, e.bm);
+    args.tiles_n = (int)ceil_div(N, e.bn);
+    args.k_tiles = (int)ceil_div(K, cfg_bk(e));
+    args.vec_ok = aligned_operands(dtype, A, lda, B, ldb) ? 1 : 0;
+    const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
+    if (grid > INT32_MAX) return TDG_ERR_UNSUPPORTED;
+
+    void *kargs[] = {&args};
+    hipError_t err = hipLaunchKernel(e.fn, dim3((unsigned)grid), dim3((unsigned)e.threads), kargs,
+                                     0, (hipStream_t)stream);
+    if (err != hipSuccess) return TDG_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess) return TDG_ERR_LAUNCH;
+    return TDG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
+                int64_t ldb, float *C, int64_t ldc, void *stream) {
+    tdg_config cfg;
+    memset(&cfg, 0, sizeof(cfg));
+    cfg.variant = TDG_VARIANT_SINGLE;
+    return run(TDG_DTYPE_F16F32, M, N, K, A, lda, B, ldb, C, ldc, stream, &cfg, false);
+}
+
+int gemm_i8i32(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const int8_t *B,
+               int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
+    tdg_config cfg;
+    memset(&cfg, 0, sizeof(cfg));
+    cfg.variant = TDG_VARIANT_SINGLE;
+    return run(TDG_DTYPE_I8I32, M, N, K, A, lda, B, ldb, C, ldc, stream, &cfg, false);
+}
+
+int gemm_f16f32_pipelined(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                          const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+    return run(TDG_DTYPE_F16F32, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr, true);
+}
+
+int gemm_i8i32_pipelined(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                         const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream) {
+    return run(TDG_DTYPE_I8I32, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr, true);
+}
+
+int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream,
+                   const tdg_config *cfg) {
+    return run(TDG_DTYPE_F16F32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, true);
+}
+
+int gemm_i8i32_ex(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const int8_t *B,
+                  int64_t ldb, int32_t *C, int64_t ldc, void *stream, const tdg_config *cfg) {
+    return run(TDG_DTYPE_I8I32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, true);
+}
+
+int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info) {
+    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return TDG_ERR_INVALID_ARG;
+    tdg_config req;
+    memset(&req, 0, sizeof(req));
+    if (out) req = *out;
+    // Planning assumes dense operands (lda = K, ldb = N) at 16-byte aligned
+    // addresses; any stride or alignment the real call has is judged again
+    // when it runs.
+    const void *aligned = (const void *)(uintptr_t)4096;
+    const int64_t lda = K > 0 ? K : 1, ldb = N > 0 ? N : 1;
+    return resolve(dtype, M, N, K, aligned, lda, aligned, ldb, req, true, nullptr, out, info);
+}
+
+int tdg_config_count(int dtype) {
+    int count = 0, n = 0;
+    const KernelEntry *table = tdg::kernel_table(&count);
+    for (int i = 0; i < count; i++)
+        if (table[i].dtype == dtype && !table[i].guard) n++;
+    return n;
+}
+
+int tdg_config_at(int dtype, int index, tdg_config *out) {
+    if (!out || index < 0) return TDG_ERR_INVALID_ARG;
+    int count = 0, n = 0;
+    const KernelEntry *table = tdg::kernel_table(&count);
+    for (int i = 0; i < count; i++) {
+        const KernelEntry &e = table[i];
+        if (e.dtype != dtype || e.guard) continue;
+        if (n == index) {
+            out->bm = e.bm;
+            out->bn = e.bn;
+            out->bk = cfg_bk(e);
+            out->waves = cfg_waves(e);
+            out->lds_stages = e.stages;
+            out->variant = e.variant;
+            return TDG_OK;
+        }
+        n++;
+    }
+    return TDG_ERR_INVALID_ARG;
+}
+
+const char *tdg_status_string(int status) {
+    switch (status) {
+        case TDG_OK: return "ok";
+        case TDG_ERR_INVALID_ARG: return "invalid argument";
+        case TDG_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TDG_ERR_LAUNCH: return "kernel launch failed";
+        case TDG_ERR_NO_DEVICE: return "no gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

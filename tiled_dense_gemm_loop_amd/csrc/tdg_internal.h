@@ -1,0 +1,25 @@
+// tdg_internal.h -- declarations shared by the kernel table and the host API.
+#pragma once
+
+namespace tdg {
+
+// One built kernel: its tile shape, loop form and launch needs.
+struct KernelEntry {
+    int dtype;      // 0 = FP16 -> FP32, 1 = INT8 -> INT32
+    int bm, bn;     // C tile
+    int bkb;        // K tile in bytes per row (BK = bkb / sizeof(T))
+    int wm, wn;     // wave grid; waves = wm * wn
+    int stages;     // LDS buffers
+    int variant;    // 1 sequential, 2 register prefetch, 3 direct-to-LDS
+    bool guard;     // bounds-checked loads and stores
+    const void *fn; // __global__ function
+    int threads;    // workgroup size
+    int lds_bytes;  // static LDS per workgroup
+};
+
+// Per-dtype tables (one translation unit each) and their concatenation.
+const KernelEntry *kernel_table_f16(int *count);
+const KernelEntry *kernel_table_i8(int *count);
+const KernelEntry *kernel_table(int *count);
+
+}  // namespace tdg

@@ -1,0 +1,48 @@
+// tdg_kernels.hip -- the built-in kernel configurations and their table.
+//
+// Each tile shape (BM x BN, K tile of BKB bytes, WM x WN waves) is built for
+// both dtypes in six forms: the sequential baseline, the register-prefetch
+// loop with one and with two LDS buffers, the direct-to-LDS loop, and the
+// bounds-checked forms of the baseline and of the double-buffered
+// register-prefetch loop (used for ragged or misaligned operands).
+#include "tdg_internal.h"
+#include "tdg_kernels.hpp"
+
+namespace tdg {
+
+#define TDG_ENTRY(DT, BM, BN, BKB, WM, WN, ST, VAR, GUARD)                                        \
+    KernelEntry{DT, BM, BN, BKB, WM, WN, ST, VAR, GUARD,                                         \
+                (const void *)&tdg_gemm_kernel<DT, BM, BN, BKB, WM, WN, ST, VAR, GUARD>,         \
+                WM * WN * 64, ST * Geo<DT, BM, BN, BKB, WM, WN>::STAGE_BYTES}
+
+#define TDG_SHAPE(DT, BM, BN, BKB, WM, WN)                                  \
+    TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 1, VAR_SINGLE, false),               \
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 1, VAR_REG, false),              \
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_REG, false),              \
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_DIRECT, false),           \
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 1, VAR_SINGLE, true),            \
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_REG, true)
+
+#define TDG_SHAPES(DT)                               \
+    TDG_SHAPE(DT, 256, 256, 128, 2, 2),              \
+        TDG_SHAPE(DT, 256, 256, 128, 2, 4),          \
+        TDG_SHAPE(DT, 256, 256, 64, 2, 2),           \
+        TDG_SHAPE(DT, 256, 128, 128, 2, 2),          \
+        TDG_SHAPE(DT, 128, 128, 128, 2, 2),          \
+        TDG_SHAPE(DT, 128, 64, 128, 4, 1),           \
+        TDG_SHAPE(DT, 64, 64, 128, 2, 2)
+
+// Each dtype's table is its own translation unit (TDG_BUILD_DT = 0 or 1), so
+// the two halves compile in parallel.
+#if TDG_BUILD_DT == 0
+static const KernelEntry kTable[] = {TDG_SHAPES(DT_F16)};
+const KernelEntry *kernel_table_f16(int *count) {
+#else
+static const KernelEntry kTable[] = {TDG_SHAPES(DT_I8)};
+const KernelEntry *kernel_table_i8(int *count) {
+#endif
+    *count = (int)(sizeof(kTable) / sizeof(kTable[0]));
+    return kTable;
+}
+
+}  // namespace tdg

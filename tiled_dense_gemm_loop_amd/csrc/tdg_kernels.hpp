@@ -1,0 +1,414 @@
+// tdg_kernels.hpp -- gfx950 (CDNA4) tiled dense GEMM kernels, C = A . B.
+//
+// One kernel template covers the sequential baseline and the two pipelined
+// variants of "Pipeline GPU Kernel":
+//   VAR_SINGLE  -- Step 1's sequential K loop: load tile t to registers, wait,
+//                  barrier, write LDS, barrier, compute on it.
+//   VAR_REG     -- Step 2/3's register-prefetch variant: the global loads of
+//                  tile t+1 go to registers and are in flight while the matrix
+//                  cores work on tile t; the registers are then drained into
+//                  the other LDS buffer (STAGES = 2), or, with STAGES = 1,
+//                  into the same buffer after a barrier (Step 1, "Expected
+//                  result on failure": register-only prefetch).
+//   VAR_DIRECT  -- Step 2/3's asynchronous-copy variant, done with gfx950's
+//                  global-to-LDS DMA (global_load_lds_dwordx4): tile t+1 is
+//                  copied straight into the other LDS buffer without passing
+//                  through registers; "wait for the copies" is
+//                  s_waitcnt vmcnt(0) followed by the barrier.
+// All three share the prologue / main loop / epilogue shape of Step 3 and the
+// buffer discipline of Step 3's failure note: compute reads buffer t % S,
+// loads write buffer (t + 1) % S, the epilogue computes buffer
+// (num_tiles - 1) % S.
+//
+// Tile micro-kernel: each wave owns a (BM/WM) x (BN/WN) block of C held in
+// 32x32 MFMA accumulators (v_mfma_f32_32x32x16_f16 / v_mfma_i32_32x32x32_i8).
+// The K tile is BKB bytes of every row (64 FP16 or 128 INT8 elements at
+// BKB = 128).  A is kept in LDS row-major (K contiguous) and read with
+// ds_read_b128; B is kept in LDS as it sits in memory (N contiguous) and read
+// with gfx950's transposing ds_read_b64_tr_b16 / ds_read_b64_tr_b8, which
+// hands each lane the K-contiguous column slice the MFMA B operand wants.
+// Both LDS images use 16-byte-chunk XOR swizzles chosen for gfx950's 64 banks
+// (256 bytes per cycle), so that the fragment reads, the register drains and
+// the DMA writes are free of bank conflicts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define TDG_LDS __attribute__((address_space(3)))
+#define TDG_GLOBAL __attribute__((address_space(1)))
+
+enum { DT_F16 = 0, DT_I8 = 1 };
+enum { VAR_SINGLE = 1, VAR_REG = 2, VAR_DIRECT = 3 };
+
+// Kernel arguments (passed by value).  Leading dimensions are in elements.
+struct GemmArgs {
+    const unsigned char *A;
+    const unsigned char *B;
+    unsigned char *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int k_tiles;  // ceil(K / BK); 0 when K == 0 (C is then zero-filled)
+    int vec_ok;   // 1 when every full 16-byte chunk of A and B is 16-byte aligned
+};
+
+// Compile-time geometry of one configuration.
+template <int DT, int BM_, int BN_, int BKB_, int WM_, int WN_>
+struct Geo {
+    static constexpr int ES = DT == DT_F16 ? 2 : 1;  // input element bytes
+    static constexpr int BM = BM_, BN = BN_, BKB = BKB_;
+    static constexpr int BK = BKB / ES;  // K elements per tile
+    static constexpr int WM = WM_, WN = WN_;
+    static constexpr int NWAVES = WM * WN, NT = NWAVES * 64;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+    static constexpr int MI = WTM / 32, NI = WTN / 32;  // 32x32 MFMA blocks per wave
+    static constexpr int KSTEPS = BKB / 32;             // MFMA K steps per tile (32 bytes each)
+    // A image: BM rows of BKB bytes.
+    static constexpr int A_CPR = BKB / 16;
+    static constexpr int A_CHUNKS = BM * A_CPR;
+    static constexpr int A_BYTES = BM * BKB;
+    static constexpr int A_RP = 256 / BKB;  // A rows per 256-byte bank line
+    // B image: BK rows (k) of BN*ES bytes.
+    static constexpr int B_ROWB = BN * ES;
+    static constexpr int B_CPR = B_ROWB / 16;
+    static constexpr int B_CHUNKS = BK * B_CPR;
+    static constexpr int B_BYTES = BK * B_ROWB;
+    static constexpr int B_RP = B_ROWB >= 256 ? 1 : 256 / B_ROWB;
+    // Transposed-read geometry: a 16-lane group reads TR_ROWS k-rows, LPR lanes
+    // per row, EPL elements per lane; two adjacent groups read SEG_CH chunks.
+    static constexpr int TR_ROWS = DT == DT_F16 ? 4 : 8;
+    static constexpr int LPR = 16 / TR_ROWS;
+    static constexpr int EPL = 8 / ES;
+    static constexpr int SEG_CH = DT == DT_F16 ? 4 : 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int CA = A_CHUNKS / NT;  // A chunks per thread per tile
+    static constexpr int CB = B_CHUNKS / NT;  // B chunks per thread per tile
+
+    static_assert(BKB == 64 || BKB == 128, "K tile is 64 or 128 bytes per row");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "tile must split evenly over threads");
+    static_assert((B_CPR & (B_CPR - 1)) == 0, "B row must be a power-of-two number of chunks");
+    static_assert(TR_ROWS >= B_RP, "B rows per bank line exceed the transposed-read group");
+    static_assert(SEG_CH * (TR_ROWS / B_RP) <= B_CPR, "B swizzle must stay inside a row");
+
+    // Physical 16-byte chunk of logical chunk c in A row r.  Sixteen
+    // consecutive rows read at one logical chunk land on 16 distinct
+    // 16-byte bank slots of the 256-byte bank line.
+    __device__ static __forceinline__ int swz_a(int r) { return (r / A_RP) % A_CPR; }
+    // XOR applied to the chunk index of B row k: the TR_ROWS rows that one
+    // transposed read touches, SEG_CH chunks each, land on distinct slots.
+    __device__ static __forceinline__ int swz_b(int k) {
+        return ((k / B_RP) % (TR_ROWS / B_RP)) * SEG_CH;
+    }
+};
+
+// MFMA operand/accumulator types per dtype.
+template <int DT>
+struct Mfma;
+template <>
+struct Mfma<DT_F16> {
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    __device__ static __forceinline__ acc_t mac(u32x4 a, u32x4 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    // Two transposed 8-byte reads give a lane its 8 K-consecutive halves.
+    __device__ static __forceinline__ u32x4 read_b(const unsigned char *p0, const unsigned char *p1) {
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TDG_LDS i16x4 *)(p0));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TDG_LDS i16x4 *)(p1));
+        i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+        return u32x4{(uint32_t)l2[0], (uint32_t)l2[1], (uint32_t)h2[0], (uint32_t)h2[1]};
+    }
+};
+template <>
+struct Mfma<DT_I8> {
+    typedef i32x16 acc_t;
+    typedef int32_t out_t;
+    __device__ static __forceinline__ acc_t mac(u32x4 a, u32x4 b, acc_t c) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                     __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
+    // Two transposed 8-byte reads give a lane its 16 K-consecutive bytes.
+    __device__ static __forceinline__ u32x4 read_b(const unsigned char *p0, const unsigned char *p1) {
+        i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TDG_LDS i32x2 *)(p0));
+        i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TDG_LDS i32x2 *)(p1));
+        return u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
+    }
+};
+
+__device__ static __forceinline__ u32x4 lds_read16(const unsigned char *p) {
+    return *(const TDG_LDS u32x4 *)(p);
+}
+__device__ static __forceinline__ void lds_write16(unsigned char *p, u32x4 v) {
+    *(TDG_LDS u32x4 *)(p) = v;
+}
+
+// Workgroup -> C tile.  Workgroups are dealt round-robin to the 8 XCDs, so
+// when the tile count is a multiple of 8, workgroup b is renumbered so that
+// each XCD receives a contiguous run of tile ids; the ids are then laid out in
+// groups of GROUP_M tile rows, which gives every XCD a compact block of C
+// tiles and lets its L2 reuse both A row panels and B column panels.
+__device__ static __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int &tm, int &tn) {
+    constexpr int GROUP_M = 4;
+    const int total = tiles_m * tiles_n;
+    int id = bid;
+    if ((total & 7) == 0) id = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int per_group = GROUP_M * tiles_n;
+    const int group = id / per_group;
+    const int first_m = group * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int r = id - group * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+// One 16-byte chunk, bounds-checked: elements at and beyond `valid` (and all
+// elements when `row_ok` is false) read as zero; `vec` allows one 16-byte
+// load when the whole chunk is valid.
+template <int ES>
+__device__ static __forceinline__ u32x4 load_chunk_guarded(const unsigned char *p, bool row_ok,
+                                                           int valid, bool vec) {
+    constexpr int EPC = 16 / ES;
+    if (row_ok && vec && valid >= EPC) return *(const u32x4 *)p;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (row_ok) {
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            if (e < valid) {
+                uint32_t v = ES == 2 ? (uint32_t)((const uint16_t *)p)[e] : (uint32_t)p[e];
+                w[(e * ES) >> 2] |= v << (((e * ES) & 3) * 8);
+            }
+        }
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int DT, int BM, int BN, int BKB, int WM, int WN, int STAGES, int VAR, bool GUARD>
+__global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args) {
+    typedef Geo<DT, BM, BN, BKB, WM, WN> G;
+    typedef Mfma<DT> MM;
+    typedef typename MM::acc_t acc_t;
+    typedef typename MM::out_t out_t;
+    static_assert(STAGES == 1 || STAGES == 2, "one or two LDS buffers");
+    static_assert(VAR != VAR_DIRECT || (STAGES == 2 && !GUARD),
+                  "direct-to-LDS runs double-buffered on the aligned fast path only");
+    static_assert(VAR != VAR_SINGLE || STAGES == 1, "the sequential baseline has one buffer");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * G::STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+
+    int tm, tn;
+    map_tile(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nt = args.k_tiles;
+
+    // Chunk i of this thread sits at LDS slot i*NT + tid of the A (or B)
+    // image, i.e. image row i*RSTEP + tid/CPR and physical chunk tid % CPR.
+    // The thread fetches the logical chunk that the swizzle puts there; the
+    // swizzle of a row repeats every RSTEP rows, so one 32-bit per-lane
+    // offset serves every i and every K tile, and the row/K advance goes into
+    // a wave-uniform (SGPR) base address.  The same slots serve the register
+    // drains and the LDS DMA, whose destinations are lane-contiguous.
+    constexpr int A_RSTEP = G::NT / G::A_CPR;
+    constexpr int B_RSTEP = G::NT / G::B_CPR;
+    static_assert(A_RSTEP % (G::A_RP * G::A_CPR) == 0, "A swizzle must repeat every RSTEP rows");
+    static_assert(B_RSTEP % G::TR_ROWS == 0, "B swizzle must repeat every RSTEP rows");
+    const int64_t lda_b = args.lda * G::ES, ldb_b = args.ldb * G::ES;
+    const unsigned char *a_base = args.A + (int64_t)m0 * lda_b;
+    const unsigned char *b_base = args.B + (int64_t)n0 * G::ES;
+    const int a_r0 = tid / G::A_CPR, b_k0 = tid / G::B_CPR;
+    const int a_c = (tid % G::A_CPR) ^ G::swz_a(a_r0);
+    const int b_c = (tid % G::B_CPR) ^ G::swz_b(b_k0);
+    const uint32_t a_voff = (uint32_t)(a_r0 * lda_b + a_c * 16);
+    const uint32_t b_voff = (uint32_t)(b_k0 * ldb_b + b_c * 16);
+    const uint32_t slot = (uint32_t)tid * 16u;
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)(TDG_LDS unsigned char *)smem;
+
+    // Per-lane LDS read offsets of the MFMA fragments (within one stage).
+    uint32_t a_roff[G::KSTEPS];
+    {
+        const int r = wm * G::WTM + (lane & 31);
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; s++)
+            a_roff[s] = (uint32_t)(r * G::BKB + (((2 * s + (lane >> 5)) ^ G::swz_a(r)) * 16));
+    }
+    uint32_t b_roff[G::KSTEPS][2][G::NI];
+    {
+        constexpr int KS = 32 / G::ES;       // k per MFMA step
+        constexpr int KH = KS / 2;           // k per lane half (lane / 32)
+        constexpr int KR = G::TR_ROWS;       // k per transposed read
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; s++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int k = s * KS + (lane >> 5) * KH + h * KR + (lane & 15) / G::LPR;
+#pragma unroll
+                for (int ni = 0; ni < G::NI; ni++) {
+                    const int n = wn * G::WTN + ni * 32 + ((lane >> 4) & 1) * 16 +
+                                  (lane % G::LPR) * G::EPL;
+                    const int byte = n * G::ES;
+                    b_roff[s][h][ni] = (uint32_t)(G::A_BYTES + k * G::B_ROWB +
+                                                  (((byte >> 4) ^ G::swz_b(k)) << 4) + (byte & 15));
+                }
+            }
+    }
+
+    acc_t acc[G::MI][G::NI];
+#pragma unroll
+    for (int mi = 0; mi < G::MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < G::NI; ni++) acc[mi][ni] = acc_t{};
+
+    // ---- building blocks ---------------------------------------------------
+    u32x4 ra[G::CA], rb[G::CB];  // register staging (SINGLE / REG)
+
+    auto a_ptr = [&](int kt, int i) {
+        return a_base + (int64_t)kt * G::BKB + (int64_t)(i * A_RSTEP) * lda_b;
+    };
+    auto b_ptr = [&](int kt, int i) {
+        return b_base + (int64_t)(kt * G::BK + i * B_RSTEP) * ldb_b;
+    };
+    auto load_regs = [&](int kt) {
+        if (!GUARD) {
+#pragma unroll
+            for (int i = 0; i < G::CA; i++) ra[i] = *(const u32x4 *)(a_ptr(kt, i) + a_voff);
+#pragma unroll
+            for (int i = 0; i < G::CB; i++) rb[i] = *(const u32x4 *)(b_ptr(kt, i) + b_voff);
+        } else {
+            const bool vec = args.vec_ok != 0;
+            const int kbase = kt * G::BK;
+            constexpr int EPC = 16 / G::ES;
+#pragma unroll
+            for (int i = 0; i < G::CA; i++) {
+                const bool row_ok = m0 + i * A_RSTEP + a_r0 < args.M;
+                const int valid = args.K - (kbase + a_c * EPC);
+                ra[i] = load_chunk_guarded<G::ES>(a_ptr(kt, i) + a_voff, row_ok, valid, vec);
+            }
+#pragma unroll
+            for (int i = 0; i < G::CB; i++) {
+                const bool row_ok = kbase + i * B_RSTEP + b_k0 < args.K;
+                const int valid = args.N - (n0 + b_c * EPC);
+                rb[i] = load_chunk_guarded<G::ES>(b_ptr(kt, i) + b_voff, row_ok, valid, vec);
+            }
+        }
+    };
+    auto store_regs = [&](unsigned char *st) {
+#pragma unroll
+        for (int i = 0; i < G::CA; i++) lds_write16(st + slot + i * G::NT * 16, ra[i]);
+#pragma unroll
+        for (int i = 0; i < G::CB; i++) lds_write16(st + G::A_BYTES + slot + i * G::NT * 16, rb[i]);
+    };
+    // LDS DMA: each lane's 16 bytes land at M0 + 16 * lane.  Issued from
+    // inline assembly so that the compiler does not guard the other buffer's
+    // LDS reads with a wait on these copies; completion is awaited
+    // explicitly (vmcnt) before the barrier that publishes the tile.
+    auto issue_direct = [&](uint32_t st_off, int kt) {
+        const uint32_t wbase = smem_addr + st_off + (uint32_t)wave * 1024u;
+#pragma unroll
+        for (int i = 0; i < G::CA; i++) {
+            const uint32_t m0v = wbase + (uint32_t)(i * G::NT * 16);
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(a_voff), "s"(a_ptr(kt, i)),
+                         "{m0}"(m0v)
+                         : "memory");
+        }
+#pragma unroll
+        for (int i = 0; i < G::CB; i++) {
+            const uint32_t m0v = wbase + (uint32_t)(G::A_BYTES + i * G::NT * 16);
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(b_voff), "s"(b_ptr(kt, i)),
+                         "{m0}"(m0v)
+                         : "memory");
+        }
+    };
+    auto compute = [&](const unsigned char *st) {
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; s++) {
+            u32x4 af[G::MI], bf[G::NI];
+#pragma unroll
+            for (int mi = 0; mi < G::MI; mi++) af[mi] = lds_read16(st + a_roff[s] + mi * 32 * G::BKB);
+#pragma unroll
+            for (int ni = 0; ni < G::NI; ni++)
+                bf[ni] = MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
+#pragma unroll
+            for (int mi = 0; mi < G::MI; mi++)
+#pragma unroll
+                for (int ni = 0; ni < G::NI; ni++) acc[mi][ni] = MM::mac(af[mi], bf[ni], acc[mi][ni]);
+        }
+    };
+
+    // ---- K loop ------------------------------------------------------------
+    if (nt > 0) {
+        if (VAR == VAR_SINGLE) {
+            // Sequential: load -> barrier -> compute -> barrier, every tile.
+            for (int t = 0; t < nt; t++) {
+                load_regs(t);
+                if (t > 0) __syncthreads();  // everyone finished computing on the buffer
+                store_regs(smem);
+                __syncthreads();
+                compute(smem);
+            }
+        } else if (VAR == VAR_REG) {
+            // Prologue: tile 0 into buffer 0.
+            load_regs(0);
+            store_regs(smem);
+            __syncthreads();
+            // Main loop: tiles 0 .. nt-2 computed, tiles 1 .. nt-1 loaded.
+            for (int t = 0; t < nt - 1; t++) {
+                load_regs(t + 1);  // global loads in flight during compute
+                __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the MFMAs
+                compute(smem + (t % STAGES) * G::STAGE_BYTES);
+                if (STAGES == 1) __syncthreads();  // compute done before overwrite
+                store_regs(smem + ((t + 1) % STAGES) * G::STAGE_BYTES);
+                __syncthreads();  // drained tile visible to every wave
+            }
+            // Epilogue: the last tile.
+            compute(smem + ((nt - 1) % STAGES) * G::STAGE_BYTES);
+        } else {
+            // Prologue: DMA tile 0 into buffer 0, wait, barrier.
+            issue_direct(0u, 0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+            for (int t = 0; t < nt - 1; t++) {
+                issue_direct((uint32_t)(((t + 1) & 1) * G::STAGE_BYTES), t + 1);  // in flight ...
+                compute(smem + (t & 1) * G::STAGE_BYTES);  // ... during compute
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // copies of tile t+1 landed
+                __syncthreads();
+            }
+            compute(smem + ((nt - 1) & 1) * G::STAGE_BYTES);
+        }
+    }
+
+    // ---- C write-back: 32x32 accumulator layout -> row-major C -------------
+    // lane l of block (mi, ni) holds rows 8*(v/4) + 4*(l/32) + v%4, column l%32.
+    out_t *C = (out_t *)args.C;
+    const int col_l = lane & 31, rq = (lane >> 5) * 4;
+#pragma unroll
+    for (int mi = 0; mi < G::MI; mi++)
+#pragma unroll
+        for (int ni = 0; ni < G::NI; ni++) {
+            const int col = n0 + wn * G::WTN + ni * 32 + col_l;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int row = m0 + wm * G::WTM + mi * 32 + (v >> 2) * 8 + rq + (v & 3);
+                if (!GUARD || (row < args.M && col < args.N))
+                    C[(int64_t)row * args.ldc + col] = acc[mi][ni][v];
+            }
+        }
+}
+
+}  // namespace tdg
