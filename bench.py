@@ -33,6 +33,18 @@ PEAK = {"f16": 2500.0, "i8": 5000.0}   # dense MFMA, TFLOP/s and TOP/s
 HBM_PEAK_GBS = 8000.0
 
 
+def balance_point(peak_gops: float, bw_gbs: float) -> float:
+    """Machine balance in operations per byte: peak compute / peak bandwidth
+    ("Analyze Kernel Bottleneck", Step 2)."""
+    return peak_gops / bw_gbs
+
+
+def roofline_bound(ops: float, alg_bytes: float, peak_gops: float, bw_gbs: float) -> str:
+    """'hbm' when the arithmetic intensity (operations per unique byte of HBM
+    traffic) is below the machine balance, else 'mfma'."""
+    return "hbm" if ops / alg_bytes < balance_point(peak_gops, bw_gbs) else "mfma"
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)

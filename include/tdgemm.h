@@ -74,7 +74,9 @@ typedef enum {
 
 /* One kernel configuration.  bk is in elements (64 for FP16, 128 for INT8 at
  * the default 128-byte K tile); waves is the wavefront count per workgroup
- * (64 lanes each); lds_stages is 1 or 2. */
+ * (64 lanes each); lds_stages is the number of LDS tile buffers: 1 for the
+ * sequential loop, 1 or 2 for register prefetch, 2 to 8 for direct-to-LDS
+ * (a ring with lds_stages - 1 tiles in flight). */
 typedef struct {
     int bm, bn, bk, waves, lds_stages, variant;
 } tdg_config;
@@ -135,6 +137,17 @@ int gemm_i8i32_ex(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
  * request.  Writes the result to *out and its figures to *info (either may be
  * NULL).  Host-only arithmetic: needs no device. */
 int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info);
+
+/* The planner's arithmetic for any tile, built or not: the compute/load
+ * ratio and its band, the LDS bytes of `stages` buffers ("Pipeline GPU
+ * Kernel", Step 1 and Step 2), the workgroups per MI355X compute unit (LDS,
+ * wave-slot and register limits; "Analyze Kernel Bottleneck", Step 3 and
+ * Step 6), and num_tiles / grid for an M x N x K product.  bk is in
+ * elements; variant only affects the register estimate (register staging).
+ * Host-only; returns TDG_ERR_INVALID_ARG for non-positive tile sizes or
+ * waves, stages outside 1..8, or negative M, N, K. */
+int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant,
+                     int64_t M, int64_t N, int64_t K, tdg_plan_info *info);
 
 /* Number of built-in kernel configurations for a dtype, and the i-th one. */
 int tdg_config_count(int dtype);

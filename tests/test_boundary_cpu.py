@@ -1,0 +1,152 @@
+"""CPU tests of the C-ABI library: it loads without a GPU, exports every
+symbol include/tdgemm.h declares, rejects bad arguments before touching the
+device, and its planner arithmetic reproduces the pages' worked examples
+(tests/golden/pages_worked_examples.json).  No GEMM is computed here."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_loop_amd as tdg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_worked_examples.json")))
+DT = {"f16": tdg.TDG_DTYPE_F16F32, "i8": tdg.TDG_DTYPE_I8I32}
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tdgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = tdg.load_library()
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(tdg.EXPORTED) == declared
+
+
+def test_status_strings():
+    assert tdg.tdg_status_string(tdg.TDG_OK) == "ok"
+    assert "invalid" in tdg.tdg_status_string(tdg.TDG_ERR_INVALID_ARG)
+    assert tdg.tdg_status_string(12345) == "unknown status"
+
+
+# --- argument validation runs before any HIP call ----------------------------------
+
+BAD_CALLS = [
+    ("negative M", (-1, 4, 4, 4096, 4, 8192, 4, 1 << 20, 4)),
+    ("negative K", (4, 4, -2, 4096, 4, 8192, 4, 1 << 20, 4)),
+    ("lda < K", (4, 4, 8, 4096, 4, 8192, 4, 1 << 20, 4)),
+    ("ldb < N", (4, 8, 4, 4096, 4, 8192, 4, 1 << 20, 8)),
+    ("ldc < N", (4, 8, 4, 4096, 4, 8192, 8, 1 << 20, 4)),
+    ("NULL A", (4, 4, 4, 0, 4, 8192, 4, 1 << 20, 4)),
+    ("NULL B", (4, 4, 4, 4096, 4, 0, 4, 1 << 20, 4)),
+    ("NULL C", (4, 4, 4, 4096, 4, 8192, 4, 0, 4)),
+    ("C overlaps A", (4, 4, 4, 4096, 4, 1 << 20, 4, 4096 + 8, 4)),
+    ("C overlaps B", (4, 4, 4, 1 << 20, 4, 8192, 4, 8192 - 16, 4)),
+    ("M too large", (1 << 31, 4, 4, 4096, 4, 8192, 4, 1 << 40, 4)),
+]
+
+
+@pytest.mark.parametrize("name", ["gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined",
+                                  "gemm_i8i32_pipelined", "gemm_f16f32_ex", "gemm_i8i32_ex"])
+@pytest.mark.parametrize("what,args", BAD_CALLS, ids=[b[0] for b in BAD_CALLS])
+def test_invalid_arguments(name, what, args):
+    assert tdg.call_raw(name, *args) == tdg.TDG_ERR_INVALID_ARG
+
+
+def test_empty_output_returns_ok_without_a_device():
+    # M == 0 or N == 0: nothing to do, no device needed
+    assert tdg.call_raw("gemm_f16f32_pipelined", 0, 4, 4, 0, 4, 8192, 4, 0, 4) == tdg.TDG_OK
+    assert tdg.call_raw("gemm_i8i32", 4, 0, 4, 4096, 4, 0, 1, 0, 1) == tdg.TDG_OK
+
+
+def test_unbuilt_configuration_is_unsupported():
+    cfg = tdg.TdgConfig(bm=96, bn=96, bk=0, waves=0, lds_stages=0, variant=0)
+    with pytest.raises(tdg.TdgError) as e:
+        tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4096, 4096, 4096, cfg)
+    assert e.value.status == tdg.TDG_ERR_UNSUPPORTED
+    cfg = tdg.TdgConfig(bm=0, bn=0, bk=0, waves=0, lds_stages=3, variant=tdg.TDG_VARIANT_SINGLE)
+    with pytest.raises(tdg.TdgError):
+        tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4096, 4096, 4096, cfg)
+
+
+# --- planner arithmetic pinned to the pages -------------------------------------------
+
+@pytest.mark.parametrize("case", GOLDEN["lds_budget"], ids=lambda c: "%s_%dx%dx%d_s%d" % (
+    c["dtype"], c["bm"], c["bn"], c["bk"], c["stages"]))
+def test_lds_budget_matches_the_pages(case):
+    info = tdg.tdg_tile_figures(DT[case["dtype"]], case["bm"], case["bn"], case["bk"],
+                                stages=case["stages"])
+    assert info["lds_bytes"] == case["lds_bytes"]
+
+
+def test_doubling_doubles():
+    for c in GOLDEN["lds_budget"]:
+        one = tdg.tdg_tile_figures(DT[c["dtype"]], c["bm"], c["bn"], c["bk"], stages=1)
+        two = tdg.tdg_tile_figures(DT[c["dtype"]], c["bm"], c["bn"], c["bk"], stages=2)
+        assert two["lds_bytes"] == 2 * one["lds_bytes"]
+
+
+@pytest.mark.parametrize("case", GOLDEN["balance_points"], ids=lambda c: str(c["balance"]))
+def test_balance_points_match_the_pages(case):
+    import bench
+    assert round(bench.balance_point(case["peak_gops"], case["bw_gbs"]), 1) == case["balance"]
+
+
+def test_ratio_formula_and_bands():
+    # ratio = 2*BM*BN*BK / ((BM*BK + BK*BN) * sizeof(T)), i.e. BM*BN/(BM+BN) for FP16
+    for (bm, bn, bk) in [(256, 256, 64), (128, 64, 32), (16, 16, 16), (8, 8, 8), (3, 5, 7)]:
+        f16 = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, bm, bn, bk)
+        i8 = tdg.tdg_tile_figures(tdg.TDG_DTYPE_I8I32, bm, bn, bk)
+        assert f16["ratio"] == pytest.approx(2 * bm * bn * bk / ((bm * bk + bk * bn) * 2))
+        assert i8["ratio"] == pytest.approx(2 * f16["ratio"])
+    bands = {(8, 8, 8): 0, (16, 16, 16): 1, (40, 40, 40): 1, (42, 42, 16): 2, (256, 256, 64): 2}
+    for (bm, bn, bk), band in bands.items():
+        assert tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, bm, bn, bk)["band"] == band
+    # the boundaries themselves: ratio 5 -> band 1, ratio 20 -> band 1
+    assert tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 10, 10, 4)["ratio"] == 5.0
+    assert tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 10, 10, 4)["band"] == 1
+    assert tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 40, 40, 4)["band"] == 1
+
+
+def test_occupancy_limits_follow_the_160k_lds():
+    # 256x256 FP16 with a 64-element K tile: 64 KiB per buffer, two buffers
+    # 128 KiB -> one workgroup per CU (its 8 waves also fill the registers)
+    two = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 256, 256, 64, waves=8, stages=2)
+    assert (two["lds_bytes"], two["wg_per_cu"]) == (131072, 1)
+    # 128x128x64 FP16: 32 KiB per buffer; two buffers -> LDS allows 2 per CU,
+    # one buffer would allow 5 and the registers then decide
+    two = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 128, 128, 64, waves=4, stages=2)
+    one = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 128, 128, 64, waves=4, stages=1)
+    assert (two["lds_bytes"], two["wg_per_cu"]) == (65536, 2)
+    assert 2 < one["wg_per_cu"] <= 5
+    # 53.3 KiB is the two-per-CU cliff: 54 KiB per workgroup gives two, not three
+    assert tdg.tdg_tile_figures(tdg.TDG_DTYPE_I8I32, 128, 88, 256, stages=1)["wg_per_cu"] == 2
+
+
+def test_grid_and_trip_count():
+    info = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 256, 256, 64, 8, 2, 3, 4096, 4096, 4100)
+    assert info["grid"] == 256 and info["num_tiles"] == 65
+
+
+def test_planner_choices():
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4096, 4096, 4096)
+    assert (cfg["bm"], cfg["bn"], cfg["variant"]) == (256, 256, tdg.TDG_VARIANT_DIRECT_LDS)
+    assert info["grid"] == 256 and info["guarded"] == 0
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 16384, 64, 8192)
+    assert cfg["bn"] == 64 and cfg["lds_stages"] >= 2 and info["grid"] >= 256
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_I8I32, 300, 290, 333)
+    assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH
+    # every built configuration can be planned back exactly
+    for code in (0, 1):
+        for i in range(tdg.tdg_config_count(code)):
+            c = tdg.tdg_config_at(code, i)
+            got, _ = tdg.tdg_plan(code, 4 * c["bm"], 4 * c["bn"], 8 * c["bk"], dict(c))
+            assert got == c

@@ -42,14 +42,20 @@ def _check(dtype, C, A, B, exact=False):
 
 
 def _variants(lib, dtype, tile):
-    """All four loop forms at one tile shape: (name, cfg)."""
-    base = {"bm": tile["bm"], "bn": tile["bn"], "bk": tile["bk"], "waves": tile["waves"]}
-    return [
-        ("single", dict(base, variant=lib.TDG_VARIANT_SINGLE, lds_stages=1)),
-        ("reg_s1", dict(base, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=1)),
-        ("reg_s2", dict(base, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)),
-        ("direct", dict(base, variant=lib.TDG_VARIANT_DIRECT_LDS, lds_stages=2)),
-    ]
+    """Every built loop form (variant x LDS stages) at one tile shape:
+    [(name, cfg)], the sequential baseline first."""
+    import tiled_dense_gemm_loop_amd as t
+    code = 0 if dtype == F16 else 1
+    out = []
+    for i in range(t.tdg_config_count(code)):
+        c = t.tdg_config_at(code, i)
+        if (c["bm"], c["bn"], c["bk"], c["waves"]) != (tile["bm"], tile["bn"], tile["bk"],
+                                                        tile["waves"]):
+            continue
+        out.append(("%s_s%d" % (t.VARIANT_NAMES[c["variant"]], c["lds_stages"]), c))
+    out.sort(key=lambda nc: (nc[1]["variant"], nc[1]["lds_stages"]))
+    assert out and out[0][1]["variant"] == t.TDG_VARIANT_SINGLE
+    return out
 
 
 def _tiles(dtype_code):

@@ -35,4 +35,5 @@ from ._binding import (  # noqa: F401
     tdg_config_count,
     tdg_plan,
     tdg_status_string,
+    tdg_tile_figures,
 )

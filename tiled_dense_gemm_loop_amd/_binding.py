@@ -32,8 +32,8 @@ VARIANT_NAMES = {0: "auto", 1: "single", 2: "reg_prefetch", 3: "direct_lds"}
 # Every symbol include/tdgemm.h declares.
 EXPORTED = (
     "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
-    "gemm_f16f32_ex", "gemm_i8i32_ex", "tdg_plan", "tdg_config_count", "tdg_config_at",
-    "tdg_status_string",
+    "gemm_f16f32_ex", "gemm_i8i32_ex", "tdg_plan", "tdg_tile_figures", "tdg_config_count",
+    "tdg_config_at", "tdg_status_string",
 )
 
 
@@ -94,6 +94,9 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_plan.argtypes = [c_int, i64, i64, i64, ctypes.POINTER(TdgConfig),
                              ctypes.POINTER(TdgPlanInfo)]
     lib.tdg_plan.restype = c_int
+    lib.tdg_tile_figures.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, i64, i64,
+                                     i64, ctypes.POINTER(TdgPlanInfo)]
+    lib.tdg_tile_figures.restype = c_int
     lib.tdg_config_count.argtypes = [c_int]
     lib.tdg_config_count.restype = c_int
     lib.tdg_config_at.argtypes = [c_int, c_int, ctypes.POINTER(TdgConfig)]
@@ -211,6 +214,17 @@ def tdg_plan(dtype: int, M: int, N: int, K: int, cfg=None):
     if rc != TDG_OK:
         raise TdgError(rc, "tdg_plan")
     return c.as_dict(), info.as_dict()
+
+
+def tdg_tile_figures(dtype: int, bm: int, bn: int, bk: int, waves: int = 4, stages: int = 1,
+                     variant: int = TDG_VARIANT_SINGLE, M: int = 0, N: int = 0, K: int = 0) -> dict:
+    """The planner's arithmetic (ratio, band, LDS bytes, WG/CU, ...) for any tile."""
+    info = TdgPlanInfo()
+    rc = load_library().tdg_tile_figures(dtype, bm, bn, bk, waves, stages, variant, M, N, K,
+                                         ctypes.byref(info))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_tile_figures")
+    return info.as_dict()
 
 
 def tdg_config_count(dtype: int) -> int:

@@ -116,47 +116,72 @@ bool offsets_fit(int dtype, int64_t lda, int64_t ldb) {
     return 64 * lda * es + 256 < lim && 64 * ldb * es + 256 < lim;
 }
 
-// Estimated 32-bit registers per lane: accumulators plus staging.
-int est_regs(const KernelEntry &e, int variant) {
-    const int waves = cfg_waves(e);
-    const int acc = e.bm * e.bn / (waves * 64);
-    const int stage_bytes = (e.bm + e.bn) * e.bkb;  // one K tile of A and B
-    const int staging = variant == TDG_VARIANT_DIRECT_LDS ? 0 : stage_bytes / (waves * 64) / 4;
-    const int frags = 4 * (e.bm / e.wm / 32 + e.bn / e.wn / 32) * 2;
+// Estimated 32-bit registers per lane: accumulators, register staging of one
+// K tile (not for direct-to-LDS) and two sets of MFMA fragments.
+int est_regs(int bm, int bn, int bkb, int waves, int variant) {
+    const int lanes = waves * 64;
+    const int acc = bm * bn / lanes;
+    const int staging = variant == TDG_VARIANT_DIRECT_LDS ? 0 : (bm + bn) * bkb / lanes / 4;
+    // a wave owns about (bm * bn / waves) outputs, split into 32x32 blocks
+    const double wave_side = 32.0 * __builtin_sqrt((double)bm * bn / waves / 1024.0);
+    const int frags = 2 * 2 * 4 * (int)(wave_side / 32.0 + 0.5);
     return acc + staging + frags + 24;
+}
+
+// The pages' planning arithmetic for one tile and problem.
+void tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant, int64_t M,
+                  int64_t N, int64_t K, tdg_plan_info *info) {
+    const int es = elem_size(dtype);
+    // "Pipeline GPU Kernel", Step 2: operations per byte loaded per tile.
+    const double flops = 2.0 * bm * bn * bk;
+    const double bytes = ((double)bm * bk + (double)bk * bn) * es;
+    info->ratio = flops / bytes;
+    info->band = info->ratio < 5.0 ? 0 : (info->ratio <= 20.0 ? 1 : 2);
+    // "Pipeline GPU Kernel", Step 1: one buffer = (BM*BK + BK*BN)*sizeof(T).
+    info->lds_bytes = (size_t)stages * ((size_t)bm * bk + (size_t)bk * bn) * (size_t)es;
+    const int by_lds = info->lds_bytes ? (int)(kLdsPerCU / info->lds_bytes) : 64;
+    const int by_waves = kWaveSlotsPerCU / waves;
+    const int regs = est_regs(bm, bn, bk * es, waves, variant);
+    int waves_per_simd = kRegsPerLanePerSIMD / (regs < 1 ? 1 : regs);
+    if (waves_per_simd > 8) waves_per_simd = 8;
+    const int by_regs = waves_per_simd * 4 / waves;
+    int wg = by_lds < by_waves ? by_lds : by_waves;
+    info->wg_per_cu = wg < by_regs ? wg : by_regs;
+    info->num_tiles = ceil_div(K, bk);
+    info->grid = ceil_div(M, bm) * ceil_div(N, bn);
+    info->est_regs = regs;
+    info->guarded = 0;
 }
 
 void fill_info(const KernelEntry &e, int variant, int stages, int64_t M, int64_t N, int64_t K,
                bool guarded, tdg_plan_info *info) {
     if (!info) return;
-    const int es = elem_size(e.dtype);
-    const int bk = cfg_bk(e);
-    // "Pipeline GPU Kernel", Step 2: operations per byte loaded per tile.
-    const double flops = 2.0 * e.bm * e.bn * bk;
-    const double bytes = (double)(e.bm * bk + bk * e.bn) * es;
-    info->ratio = flops / bytes;
-    info->band = info->ratio < 5.0 ? 0 : (info->ratio <= 20.0 ? 1 : 2);
-    // "Pipeline GPU Kernel", Step 1: one buffer = (BM*BK + BK*BN)*sizeof(T).
-    info->lds_bytes = (size_t)stages * (size_t)(e.bm * bk + bk * e.bn) * (size_t)es;
-    const int waves = cfg_waves(e);
-    int by_lds = info->lds_bytes ? (int)(kLdsPerCU / info->lds_bytes) : 64;
-    int by_waves = kWaveSlotsPerCU / waves;
-    const int regs = est_regs(e, variant);
-    int waves_per_simd = kRegsPerLanePerSIMD / (regs < 1 ? 1 : regs);
-    if (waves_per_simd > 8) waves_per_simd = 8;
-    int by_regs = waves_per_simd * 4 / waves;
-    int wg = by_lds < by_waves ? by_lds : by_waves;
-    wg = wg < by_regs ? wg : by_regs;
-    info->wg_per_cu = wg;
-    info->num_tiles = ceil_div(K, bk);
-    info->grid = ceil_div(M, e.bm) * ceil_div(N, e.bn);
-    info->est_regs = regs;
+    tile_figures(e.dtype, e.bm, e.bn, cfg_bk(e), cfg_waves(e), stages, variant, M, N, K, info);
     info->guarded = guarded ? 1 : 0;
 }
 
-// Measured choice of tile shape: the largest tile that still gives every
-// compute unit a workgroup; when no tile does, the one giving the most
-// workgroups.  Skinny products (N <= 64) use the 64-column tiles.
+// Wave count and ring depth per tile shape that measured fastest for the
+// direct-to-LDS loop on MI355X (4096^3 FP16 and INT8, 16384 x 64 x 8192 FP16);
+// tiles not listed use 4 waves and a two-buffer ring.
+struct Measured {
+    int bm, bn, bkb, waves, stages;
+};
+const Measured kMeasured[] = {
+    {256, 256, 128, 8, 2},
+    {128, 64, 128, 4, 4},
+    {64, 64, 128, 4, 4},
+};
+
+const Measured *measured_for(int bm, int bn, int bkb) {
+    for (const Measured &m : kMeasured)
+        if (m.bm == bm && m.bn == bn && m.bkb == bkb) return &m;
+    return nullptr;
+}
+
+// Tile shape for a product: the largest tile that still gives every compute
+// unit a workgroup; when no tile does, the one giving the most workgroups.
+// Skinny products (N <= 64) use the 64-column tiles.  Only the 128-byte K
+// tile is chosen automatically, with the measured wave count.
 const KernelEntry *choose_tile(int dtype, int64_t M, int64_t N, int64_t K, const tdg_config &req) {
     int count = 0;
     const KernelEntry *table = tdg::kernel_table(&count);
@@ -168,9 +193,11 @@ const KernelEntry *choose_tile(int dtype, int64_t M, int64_t N, int64_t K, const
         const KernelEntry &e = table[i];
         if (e.dtype != dtype || e.guard || e.variant != TDG_VARIANT_SINGLE) continue;
         if (!tile_matches(req, e)) continue;
-        // auto selection only considers the default K tile and 4 waves
         if (req.bk == 0 && e.bkb != 128) continue;
-        if (req.waves == 0 && cfg_waves(e) != 4) continue;
+        if (req.waves == 0) {
+            const Measured *m = measured_for(e.bm, e.bn, e.bkb);
+            if (cfg_waves(e) != (m ? m->waves : 4)) continue;
+        }
         if (req.bn == 0 && N <= 64 && e.bn != 64) continue;
         const int64_t grid = ceil_div(M, e.bm) * ceil_div(N, e.bn);
         const int64_t area = (int64_t)e.bm * e.bn;
@@ -201,6 +228,15 @@ const KernelEntry *find_entry(const KernelEntry &tile, int stages, int variant, 
     return nullptr;
 }
 
+// Ring depth the direct-to-LDS loop uses when the caller leaves it open: the
+// measured best for the tile shape when there is one, else two buffers.
+int preferred_direct_stages(const KernelEntry &tile) {
+    const Measured *m = measured_for(tile.bm, tile.bn, tile.bkb);
+    if (m && m->waves == cfg_waves(tile) && find_entry(tile, m->stages, TDG_VARIANT_DIRECT_LDS, false))
+        return m->stages;
+    return 2;
+}
+
 struct Resolved {
     const KernelEntry *entry;  // kernel to launch
     int variant, stages;
@@ -213,7 +249,7 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
             tdg_config *cfg_out, tdg_plan_info *info) {
     tdg_config req = req_in;
     if (req.variant < 0 || req.variant > TDG_VARIANT_DIRECT_LDS) return TDG_ERR_INVALID_ARG;
-    if (req.lds_stages < 0 || req.lds_stages > 2) return TDG_ERR_UNSUPPORTED;
+    if (req.lds_stages < 0 || req.lds_stages > 8) return TDG_ERR_UNSUPPORTED;
     const KernelEntry *tile = choose_tile(dtype, M, N, K, req);
     if (!tile) return TDG_ERR_UNSUPPORTED;
     const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
@@ -224,9 +260,13 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         variant = pipelined_default ? (fast ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
                                     : TDG_VARIANT_SINGLE;
     int stages = req.lds_stages;
-    if (stages == 0) stages = variant == TDG_VARIANT_SINGLE ? 1 : 2;
+    if (stages == 0)
+        stages = variant == TDG_VARIANT_SINGLE ? 1
+                 : variant == TDG_VARIANT_REG_PREFETCH ? 2
+                                                       : preferred_direct_stages(*tile);
     if (variant == TDG_VARIANT_SINGLE && stages != 1) return TDG_ERR_UNSUPPORTED;
-    if (variant == TDG_VARIANT_DIRECT_LDS && stages != 2) return TDG_ERR_UNSUPPORTED;
+    if (variant == TDG_VARIANT_REG_PREFETCH && stages > 2) return TDG_ERR_UNSUPPORTED;
+    if (variant == TDG_VARIANT_DIRECT_LDS && stages < 2) return TDG_ERR_UNSUPPORTED;
 
     bool guard = !fast;
     const KernelEntry *e = nullptr;
@@ -383,6 +423,15 @@ int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_pl
     const void *aligned = (const void *)(uintptr_t)4096;
     const int64_t lda = K > 0 ? K : 1, ldb = N > 0 ? N : 1;
     return resolve(dtype, M, N, K, aligned, lda, aligned, ldb, req, true, nullptr, out, info);
+}
+
+int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant,
+                     int64_t M, int64_t N, int64_t K, tdg_plan_info *info) {
+    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (bm <= 0 || bn <= 0 || bk <= 0 || waves <= 0 || waves > 16) return TDG_ERR_INVALID_ARG;
+    if (stages < 1 || stages > 8 || M < 0 || N < 0 || K < 0 || !info) return TDG_ERR_INVALID_ARG;
+    tile_figures(dtype, bm, bn, bk, waves, stages, variant, M, N, K, info);
+    return TDG_OK;
 }
 
 int tdg_config_count(int dtype) {

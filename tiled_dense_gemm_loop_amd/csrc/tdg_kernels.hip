@@ -23,14 +23,20 @@ namespace tdg {
         TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 1, VAR_SINGLE, true),            \
         TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_REG, true)
 
-#define TDG_SHAPES(DT)                               \
-    TDG_SHAPE(DT, 256, 256, 128, 2, 2),              \
-        TDG_SHAPE(DT, 256, 256, 128, 2, 4),          \
-        TDG_SHAPE(DT, 256, 256, 64, 2, 2),           \
-        TDG_SHAPE(DT, 256, 128, 128, 2, 2),          \
-        TDG_SHAPE(DT, 128, 128, 128, 2, 2),          \
-        TDG_SHAPE(DT, 128, 64, 128, 4, 1),           \
-        TDG_SHAPE(DT, 64, 64, 128, 2, 2)
+// Deeper direct-to-LDS rings where the LDS budget allows.
+#define TDG_DIRECT(DT, BM, BN, BKB, WM, WN, ST) TDG_ENTRY(DT, BM, BN, BKB, WM, WN, ST, VAR_DIRECT, false)
+
+#define TDG_SHAPES(DT)                                                                   \
+    TDG_SHAPE(DT, 256, 256, 128, 2, 2), TDG_SHAPE(DT, 256, 256, 128, 2, 4),              \
+        TDG_SHAPE(DT, 256, 256, 64, 2, 2), TDG_DIRECT(DT, 256, 256, 64, 2, 2, 3),        \
+        TDG_DIRECT(DT, 256, 256, 64, 2, 2, 4), TDG_SHAPE(DT, 256, 256, 64, 2, 4),        \
+        TDG_DIRECT(DT, 256, 256, 64, 2, 4, 3), TDG_DIRECT(DT, 256, 256, 64, 2, 4, 4),    \
+        TDG_SHAPE(DT, 256, 128, 128, 2, 2), TDG_DIRECT(DT, 256, 128, 128, 2, 2, 3),      \
+        TDG_SHAPE(DT, 128, 128, 128, 2, 2), TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3),      \
+        TDG_DIRECT(DT, 128, 128, 128, 2, 2, 4), TDG_SHAPE(DT, 128, 64, 128, 4, 1),       \
+        TDG_DIRECT(DT, 128, 64, 128, 4, 1, 4), TDG_DIRECT(DT, 128, 64, 128, 4, 1, 6),    \
+        TDG_SHAPE(DT, 64, 64, 128, 2, 2), TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4),          \
+        TDG_DIRECT(DT, 64, 64, 128, 2, 2, 8)
 
 // Each dtype's table is its own translation unit (TDG_BUILD_DT = 0 or 1), so
 // the two halves compile in parallel.

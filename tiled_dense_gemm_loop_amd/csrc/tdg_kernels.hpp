@@ -11,10 +11,12 @@
 //                  into the same buffer after a barrier (Step 1, "Expected
 //                  result on failure": register-only prefetch).
 //   VAR_DIRECT  -- Step 2/3's asynchronous-copy variant, done with gfx950's
-//                  global-to-LDS DMA (global_load_lds_dwordx4): tile t+1 is
-//                  copied straight into the other LDS buffer without passing
-//                  through registers; "wait for the copies" is
-//                  s_waitcnt vmcnt(0) followed by the barrier.
+//                  global-to-LDS DMA (global_load_lds_dwordx4): tiles go
+//                  straight into LDS without passing through registers;
+//                  "wait for the copies" is s_waitcnt vmcnt followed by the
+//                  barrier.  With STAGES = 2 this is the pages' double
+//                  buffer; STAGES > 2 turns it into a ring with STAGES - 1
+//                  tiles in flight and partial vmcnt waits.
 // All three share the prologue / main loop / epilogue shape of Step 3 and the
 // buffer discipline of Step 3's failure note: compute reads buffer t % S,
 // loads write buffer (t + 1) % S, the epilogue computes buffer
@@ -155,6 +157,25 @@ __device__ static __forceinline__ void lds_write16(unsigned char *p, u32x4 v) {
     *(TDG_LDS u32x4 *)(p) = v;
 }
 
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left unconstrained (gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ static __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most r * IPT vector-memory operations are outstanding, for a
+// runtime r in [0, R]: each case is its own immediate.
+template <int R, int IPT>
+__device__ static __forceinline__ void wait_vmcnt_upto(int r) {
+    if constexpr (R <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (r >= R) wait_vmcnt<R * IPT>();
+        else wait_vmcnt_upto<R - 1, IPT>(r);
+    }
+}
+
 // Workgroup -> C tile.  Workgroups are dealt round-robin to the 8 XCDs, so
 // when the tile count is a multiple of 8, workgroup b is renumbered so that
 // each XCD receives a contiguous run of tile ids; the ids are then laid out in
@@ -201,9 +222,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     typedef Mfma<DT> MM;
     typedef typename MM::acc_t acc_t;
     typedef typename MM::out_t out_t;
-    static_assert(STAGES == 1 || STAGES == 2, "one or two LDS buffers");
-    static_assert(VAR != VAR_DIRECT || (STAGES == 2 && !GUARD),
-                  "direct-to-LDS runs double-buffered on the aligned fast path only");
+    static_assert(STAGES >= 1 && STAGES <= 8, "one to eight LDS buffers");
+    static_assert(VAR == VAR_DIRECT || STAGES <= 2, "register staging holds one tile");
+    static_assert(VAR != VAR_DIRECT || (STAGES >= 2 && !GUARD),
+                  "direct-to-LDS runs on the aligned fast path with two or more buffers");
+    static_assert(STAGES * G::STAGE_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
     static_assert(VAR != VAR_SINGLE || STAGES == 1, "the sequential baseline has one buffer");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * G::STAGE_BYTES];
@@ -335,61 +358,110 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                          : "memory");
         }
     };
-    auto compute = [&](const unsigned char *st) {
+    // MFMA tile micro-kernel over one LDS buffer.  The fragments of K step
+    // s+1 are requested from LDS before the MFMAs of step s are issued (two
+    // register sets, fa/fb[s & 1]), so the LDS latency hides behind a whole
+    // step of matrix work; the scheduling barriers keep the compiler from
+    // sinking the reads back next to their first use.  At the last step the
+    // loop-specific `boundary` runs before the last MFMAs: it publishes the
+    // next tile and reads that tile's first fragments into set 0, so the
+    // tile change costs no exposed LDS latency either.
+    static_assert(G::KSTEPS % 2 == 0, "fragment set parity must repeat per tile");
+    u32x4 fa[2][G::MI], fb[2][G::NI];
+    auto read_frags = [&](const unsigned char *st, int s, int set) {
 #pragma unroll
-        for (int s = 0; s < G::KSTEPS; s++) {
-            u32x4 af[G::MI], bf[G::NI];
+        for (int mi = 0; mi < G::MI; mi++) fa[set][mi] = lds_read16(st + a_roff[s] + mi * 32 * G::BKB);
 #pragma unroll
-            for (int mi = 0; mi < G::MI; mi++) af[mi] = lds_read16(st + a_roff[s] + mi * 32 * G::BKB);
+        for (int ni = 0; ni < G::NI; ni++)
+            fb[set][ni] = MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int mi = 0; mi < G::MI; mi++)
 #pragma unroll
             for (int ni = 0; ni < G::NI; ni++)
-                bf[ni] = MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
+                acc[mi][ni] = MM::mac(fa[set][mi], fb[set][ni], acc[mi][ni]);
+    };
+    // Computes the tile in buffer st; its step-0 fragments are already in set 0.
+    auto compute_tile = [&](const unsigned char *st, auto &&boundary) {
 #pragma unroll
-            for (int mi = 0; mi < G::MI; mi++)
-#pragma unroll
-                for (int ni = 0; ni < G::NI; ni++) acc[mi][ni] = MM::mac(af[mi], bf[ni], acc[mi][ni]);
+        for (int s = 0; s < G::KSTEPS; s++) {
+            if (s + 1 < G::KSTEPS) read_frags(st, s + 1, (s + 1) & 1);
+            else boundary();
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(s & 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto buf = [&](int t) { return smem + (t % STAGES) * G::STAGE_BYTES; };
 
     // ---- K loop ------------------------------------------------------------
+    // Every form has the pages' three parts: a prologue that stages tile 0
+    // (and, pipelined, the tiles after it), a main loop that computes tile t
+    // while later tiles load, and an epilogue in which the last tiles are
+    // computed with nothing left to load ("Pipeline GPU Kernel", Step 3).
     if (nt > 0) {
-        if (VAR == VAR_SINGLE) {
+        if constexpr (VAR == VAR_SINGLE) {
             // Sequential: load -> barrier -> compute -> barrier, every tile.
             for (int t = 0; t < nt; t++) {
                 load_regs(t);
                 if (t > 0) __syncthreads();  // everyone finished computing on the buffer
                 store_regs(smem);
                 __syncthreads();
-                compute(smem);
+                read_frags(smem, 0, 0);
+                compute_tile(smem, [] {});
             }
-        } else if (VAR == VAR_REG) {
+        } else if constexpr (VAR == VAR_REG) {
             // Prologue: tile 0 into buffer 0.
             load_regs(0);
             store_regs(smem);
             __syncthreads();
-            // Main loop: tiles 0 .. nt-2 computed, tiles 1 .. nt-1 loaded.
-            for (int t = 0; t < nt - 1; t++) {
-                load_regs(t + 1);  // global loads in flight during compute
-                __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the MFMAs
-                compute(smem + (t % STAGES) * G::STAGE_BYTES);
-                if (STAGES == 1) __syncthreads();  // compute done before overwrite
-                store_regs(smem + ((t + 1) % STAGES) * G::STAGE_BYTES);
-                __syncthreads();  // drained tile visible to every wave
+            read_frags(smem, 0, 0);
+            // Main loop + epilogue: tile t+1 is in registers (global loads in
+            // flight) while tile t is computed; the registers are drained into
+            // buffer (t+1) % STAGES at the tile boundary.
+            for (int t = 0; t < nt; t++) {
+                if (t + 1 < nt) load_regs(t + 1);
+                __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+                compute_tile(buf(t), [&] {
+                    if (t + 1 < nt) {
+                        if (STAGES == 1) __syncthreads();  // all reads of the buffer done
+                        store_regs(buf(t + 1));
+                        __syncthreads();  // drained tile visible to every wave
+                        read_frags(buf(t + 1), 0, 0);
+                    }
+                });
             }
-            // Epilogue: the last tile.
-            compute(smem + ((nt - 1) % STAGES) * G::STAGE_BYTES);
         } else {
-            // Prologue: DMA tile 0 into buffer 0, wait, barrier.
-            issue_direct(0u, 0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            // Ring of STAGES buffers, AHEAD = STAGES - 1 tiles in flight.
+            // Tile t lives in buffer t % STAGES; it is waited for with a
+            // partial vmcnt (younger tiles may stay in flight), published by
+            // the barrier, which also certifies that every wave has finished
+            // reading tile t - 1, whose buffer then receives tile t + AHEAD.
+            constexpr int AHEAD = STAGES - 1;
+            constexpr int IPT = G::CA + G::CB;  // DMA instructions per wave per tile
+            static_assert((AHEAD - 1) * IPT <= 63, "vmcnt holds at most 63");
+            auto stage_off = [&](int t) { return (uint32_t)((t % STAGES) * G::STAGE_BYTES); };
+            // Prologue: tiles 0 .. AHEAD-1 in flight, tile 0 published, tile
+            // AHEAD issued into the still unused last buffer.
+#pragma unroll
+            for (int p = 0; p < AHEAD; p++)
+                if (p < nt) issue_direct(stage_off(p), p);
+            wait_vmcnt_upto<AHEAD - 1, IPT>(nt - 1);
             __syncthreads();
-            for (int t = 0; t < nt - 1; t++) {
-                issue_direct((uint32_t)(((t + 1) & 1) * G::STAGE_BYTES), t + 1);  // in flight ...
-                compute(smem + (t & 1) * G::STAGE_BYTES);  // ... during compute
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // copies of tile t+1 landed
-                __syncthreads();
+            if (AHEAD < nt) issue_direct(stage_off(AHEAD), AHEAD);
+            read_frags(buf(0), 0, 0);
+            // Main loop (tiles t + AHEAD + 1 still to issue) and epilogue.
+            for (int t = 0; t < nt; t++) {
+                compute_tile(buf(t), [&] {
+                    if (t + 1 < nt) {
+                        wait_vmcnt_upto<AHEAD - 1, IPT>(nt - 2 - t);  // tile t+1 landed
+                        __syncthreads();
+                        if (t + 1 + AHEAD < nt) issue_direct(stage_off(t + 1 + AHEAD), t + 1 + AHEAD);
+                        read_frags(buf(t + 1), 0, 0);
+                    }
+                });
             }
-            compute(smem + ((nt - 1) & 1) * G::STAGE_BYTES);
         }
     }
 
