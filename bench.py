@@ -45,6 +45,28 @@ def roofline_bound(ops: float, alg_bytes: float, peak_gops: float, bw_gbs: float
     return "hbm" if ops / alg_bytes < balance_point(peak_gops, bw_gbs) else "mfma"
 
 
+def profiled_traffic(kernel_desc: str):
+    """HBM bytes per launch from a committed rocprofv3 summary in profiles/
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when no summary matches this
+    kernel configuration and the current kernel source."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "tiled_dense_gemm_loop_amd", "csrc", "tdg_kernels.hpp")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        fields = {}
+        for line in open(path):
+            for key in ("Kernel source sha256[:16]: ", "Config: "):
+                if line.startswith(key):
+                    fields[key] = line[len(key):].strip()
+            if "traffic_bytes: " in line:
+                fields["traffic"] = float(line.split("traffic_bytes: ")[1].split()[0])
+        if fields.get("Kernel source sha256[:16]: ") == digest and \
+                fields.get("Config: ") == kernel_desc and "traffic" in fields:
+            return fields["traffic"]
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
@@ -189,6 +211,10 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, A, B, args.cpu_seconds)
 
+    kernel_desc = "%dx%dx%d tile, %d waves, %d LDS stages, %s" % (
+        cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
+        tdg.VARIANT_NAMES[cfg["variant"]])
+    traffic = profiled_traffic(kernel_desc)
     line = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -204,12 +230,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
                    "accumulate": "f32" if wl.dtype == "f16" else "i32",
-                   "kernel": "%dx%dx%d tile, %d waves, %d LDS stages, %s" % (
-                       cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
-                       tdg.VARIANT_NAMES[cfg["variant"]]),
+                   "kernel": kernel_desc,
                    "parallelism": "none"},
         "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK[wl.dtype],
-                     "unit": unit, "frac": round(tops / PEAK[wl.dtype], 4), "traffic": None},
+                     "unit": unit, "frac": round(tops / PEAK[wl.dtype], 4),
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         "variants": table or None,
     }
