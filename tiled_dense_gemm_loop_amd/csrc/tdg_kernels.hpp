@@ -341,23 +341,26 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // inline assembly so that the compiler does not guard the other buffer's
     // LDS reads with a wait on these copies; completion is awaited
     // explicitly (vmcnt) before the barrier that publishes the tile.
-    auto issue_direct = [&](uint32_t st_off, int kt) {
+    auto issue_direct_one = [&](uint32_t st_off, int kt, int d) {
         const uint32_t wbase = smem_addr + st_off + (uint32_t)wave * 1024u;
-#pragma unroll
-        for (int i = 0; i < G::CA; i++) {
-            const uint32_t m0v = wbase + (uint32_t)(i * G::NT * 16);
-            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(a_voff), "s"(a_ptr(kt, i)),
+        if (d < G::CA) {
+            const uint32_t m0v = wbase + (uint32_t)(d * G::NT * 16);
+            asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(a_voff), "s"(a_ptr(kt, d)),
                          "{m0}"(m0v)
                          : "memory");
-        }
-#pragma unroll
-        for (int i = 0; i < G::CB; i++) {
+        } else {
+            const int i = d - G::CA;
             const uint32_t m0v = wbase + (uint32_t)(G::A_BYTES + i * G::NT * 16);
             asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(b_voff), "s"(b_ptr(kt, i)),
                          "{m0}"(m0v)
                          : "memory");
         }
     };
+    auto issue_direct = [&](uint32_t st_off, int kt) {
+#pragma unroll
+        for (int d = 0; d < G::CA + G::CB; d++) issue_direct_one(st_off, kt, d);
+    };
+
     // MFMA tile micro-kernel over one LDS buffer.  The fragments of K step
     // s+1 are requested from LDS before the MFMAs of step s are issued (two
     // register sets, fa/fb[s & 1]), so the LDS latency hides behind a whole
@@ -367,7 +370,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // next tile and reads that tile's first fragments into set 0, so the
     // tile change costs no exposed LDS latency either.
     static_assert(G::KSTEPS % 2 == 0, "fragment set parity must repeat per tile");
-    u32x4 fa[2][G::MI], fb[2][G::NI];
+#ifndef TDG_FRAG_DIST
+#define TDG_FRAG_DIST 2
+#endif
+    // Fragment read distance: 2 K steps ahead for the direct-to-LDS loop when
+    // a tile has 4 steps (one register set per step), else 1 (two sets); the
+    // register-prefetch loop has no room for more sets beside its staging.
+    constexpr int FD = (VAR == VAR_DIRECT && G::KSTEPS == 4) ? TDG_FRAG_DIST : 1;
+    constexpr int NSETS = FD == 1 ? 2 : G::KSTEPS;
+    static_assert(FD == 1 || NSETS == G::KSTEPS, "set index must equal the step index");
+    u32x4 fa[NSETS][G::MI], fb[NSETS][G::NI];
     auto read_frags = [&](const unsigned char *st, int s, int set) {
 #pragma unroll
         for (int mi = 0; mi < G::MI; mi++) fa[set][mi] = lds_read16(st + a_roff[s] + mi * 32 * G::BKB);
@@ -375,22 +387,66 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
         for (int ni = 0; ni < G::NI; ni++)
             fb[set][ni] = MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
     };
-    auto mfmas = [&](int set) {
+    // One K step's MFMAs with the fragment reads of a later step (read
+    // units: MI A reads, then NI pairs of transposed B reads) and, at a tile
+    // boundary, the DMA instructions of a later tile spread between them:
+    // after MFMA m come the units and DMAs whose even share falls on m.
+    // Vector-memory and LDS instructions issue in order per wave, so a burst
+    // of them from every wave at once queues and holds back each wave's next
+    // MFMAs; spread out, each one issues into an idle queue while the MFMA
+    // pipe stays busy.
+    auto step = [&](int cset, const unsigned char *rst, int rstep, int rset, bool reads,
+                    uint32_t dma_st, int dma_kt, bool dma) {
+        constexpr int NM = G::MI * G::NI, NR = G::MI + G::NI, ND = G::CA + G::CB;
 #pragma unroll
-        for (int mi = 0; mi < G::MI; mi++)
+        for (int m = 0; m < NM; m++) {
+            acc[m / G::NI][m % G::NI] =
+                MM::mac(fa[cset][m / G::NI], fb[cset][m % G::NI], acc[m / G::NI][m % G::NI]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (reads) {
 #pragma unroll
-            for (int ni = 0; ni < G::NI; ni++)
-                acc[mi][ni] = MM::mac(fa[set][mi], fb[set][ni], acc[mi][ni]);
+                for (int u = (m * NR + NM - 1) / NM; u < ((m + 1) * NR + NM - 1) / NM; u++) {
+                    if (u < G::MI) {
+                        fa[rset][u] = lds_read16(rst + a_roff[rstep] + u * 32 * G::BKB);
+                    } else {
+                        const int ni = u - G::MI;
+                        fb[rset][ni] = MM::read_b(rst + b_roff[rstep][0][ni], rst + b_roff[rstep][1][ni]);
+                    }
+                }
+            }
+            if (dma) {
+#pragma unroll
+                for (int d = (m * ND + NM - 1) / NM; d < ((m + 1) * ND + NM - 1) / NM; d++)
+                    issue_direct_one(dma_st, dma_kt, d);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    // Computes the tile in buffer st; its step-0 fragments are already in set 0.
+    auto set_of = [&](int s) { return NSETS == 2 ? (s & 1) : s; };
+    // Reads the first FD steps of the tile in buffer st.
+    auto read_first = [&](const unsigned char *st) {
+#pragma unroll
+        for (int s = 0; s < FD; s++) read_frags(st, s, set_of(s));
+    };
+    // Computes the tile in buffer st, whose first FD steps are already in
+    // registers.  `boundary` runs when the reads run past this tile: it
+    // publishes the next tile (when there is one) and returns the buffer the
+    // reads continue in -- for the last tile a buffer whose contents are
+    // never used, so the step is the same straight-line code every time.
+    // For the direct-to-LDS loop it also names the tile whose DMA is
+    // interleaved with the MFMAs of the step it runs in.
+    int dma_tile = 0;
+    uint32_t dma_off = 0;
     auto compute_tile = [&](const unsigned char *st, auto &&boundary) {
+        const unsigned char *next = st;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; s++) {
-            if (s + 1 < G::KSTEPS) read_frags(st, s + 1, (s + 1) & 1);
-            else boundary();
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(s & 1);
-            __builtin_amdgcn_sched_barrier(0);
+            const int r = s + FD;  // step whose fragments are read now
+            if (r == G::KSTEPS) next = boundary();
+            const unsigned char *rst = r < G::KSTEPS ? st : next;
+            const int rstep = r < G::KSTEPS ? r : r - G::KSTEPS;
+            step(set_of(s), rst, rstep, set_of(rstep), true, dma_off, dma_tile,
+                 VAR == VAR_DIRECT && r == G::KSTEPS);
         }
     };
     auto buf = [&](int t) { return smem + (t % STAGES) * G::STAGE_BYTES; };
@@ -408,60 +464,77 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 if (t > 0) __syncthreads();  // everyone finished computing on the buffer
                 store_regs(smem);
                 __syncthreads();
-                read_frags(smem, 0, 0);
-                compute_tile(smem, [] {});
+                read_first(smem);
+                compute_tile(smem, [&]() -> const unsigned char * { return smem; });
             }
         } else if constexpr (VAR == VAR_REG) {
             // Prologue: tile 0 into buffer 0.
             load_regs(0);
             store_regs(smem);
             __syncthreads();
-            read_frags(smem, 0, 0);
+            read_first(smem);
             // Main loop + epilogue: tile t+1 is in registers (global loads in
             // flight) while tile t is computed; the registers are drained into
             // buffer (t+1) % STAGES at the tile boundary.
             for (int t = 0; t < nt; t++) {
                 if (t + 1 < nt) load_regs(t + 1);
                 __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-                compute_tile(buf(t), [&] {
+                compute_tile(buf(t), [&]() -> const unsigned char * {
                     if (t + 1 < nt) {
                         if (STAGES == 1) __syncthreads();  // all reads of the buffer done
                         store_regs(buf(t + 1));
                         __syncthreads();  // drained tile visible to every wave
-                        read_frags(buf(t + 1), 0, 0);
                     }
+                    return buf(t + 1);
                 });
             }
         } else {
             // Ring of STAGES buffers, AHEAD = STAGES - 1 tiles in flight.
             // Tile t lives in buffer t % STAGES; it is waited for with a
-            // partial vmcnt (younger tiles may stay in flight), published by
-            // the barrier, which also certifies that every wave has finished
-            // reading tile t - 1, whose buffer then receives tile t + AHEAD.
+            // partial vmcnt (the AHEAD - 1 younger tiles stay in flight),
+            // published by the barrier, which also certifies that every wave
+            // has finished reading tile t - 1, whose buffer then receives tile
+            // t + AHEAD.  Every boundary issues exactly one tile: past the last
+            // tile it loads the last tile again into the buffer just freed,
+            // which is never read again, so the number of younger groups at
+            // every wait is AHEAD - 1 and the wait count is a constant.
             constexpr int AHEAD = STAGES - 1;
             constexpr int IPT = G::CA + G::CB;  // DMA instructions per wave per tile
             static_assert((AHEAD - 1) * IPT <= 63, "vmcnt holds at most 63");
             auto stage_off = [&](int t) { return (uint32_t)((t % STAGES) * G::STAGE_BYTES); };
+            auto src_tile = [&](int t) { return t < nt ? t : nt - 1; };
             // Prologue: tiles 0 .. AHEAD-1 in flight, tile 0 published, tile
             // AHEAD issued into the still unused last buffer.
 #pragma unroll
-            for (int p = 0; p < AHEAD; p++)
-                if (p < nt) issue_direct(stage_off(p), p);
-            wait_vmcnt_upto<AHEAD - 1, IPT>(nt - 1);
+            for (int p = 0; p < AHEAD; p++) issue_direct(stage_off(p), src_tile(p));
+            wait_vmcnt<(AHEAD - 1) * IPT>();
             __syncthreads();
-            if (AHEAD < nt) issue_direct(stage_off(AHEAD), AHEAD);
-            read_frags(buf(0), 0, 0);
-            // Main loop (tiles t + AHEAD + 1 still to issue) and epilogue.
+            issue_direct(stage_off(AHEAD), src_tile(AHEAD));
+            read_first(buf(0));
+            // Main loop and epilogue (from tile nt - AHEAD on, the issued
+            // loads are the harmless repeats).
             for (int t = 0; t < nt; t++) {
-                compute_tile(buf(t), [&] {
+                compute_tile(buf(t), [&]() -> const unsigned char * {
                     if (t + 1 < nt) {
-                        wait_vmcnt_upto<AHEAD - 1, IPT>(nt - 2 - t);  // tile t+1 landed
+                        wait_vmcnt<(AHEAD - 1) * IPT>();  // tile t+1 landed
                         __syncthreads();
-                        if (t + 1 + AHEAD < nt) issue_direct(stage_off(t + 1 + AHEAD), t + 1 + AHEAD);
-                        read_frags(buf(t + 1), 0, 0);
+                        dma_tile = src_tile(t + 1 + AHEAD);  // issued between this step's MFMAs
+                        dma_off = stage_off(t + 1 + AHEAD);
+                    } else {
+                        // last tile: no barrier; the repeat load goes to the
+                        // buffer of tile t - 1, which every wave has finished
+                        // reading (certified by the previous barrier) and
+                        // which is never read again
+                        dma_tile = nt - 1;
+                        dma_off = stage_off(t - 1 + STAGES);
                     }
+                    return buf(t + 1);
                 });
             }
+            // Drain the repeat loads before the workgroup ends: LDS written by
+            // a DMA still in flight could otherwise land in the next
+            // workgroup's allocation.
+            wait_vmcnt<0>();
         }
     }
 
