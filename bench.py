@@ -70,8 +70,10 @@ def profiled_traffic(kernel_desc: str):
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    # A launch is ~0.1 ms: 400 timed launches (~50 ms) average over the power
+    # controller's settling transient of the first few milliseconds under load.
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="fp16_4096", choices=sorted(si.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-table", action="store_true", help="skip the per-workload variant table")
@@ -190,7 +192,7 @@ def main():
                 a, b, da, db, c = device_operands(w)
             row = {}
             for variant in ("single", "reg_s1", "reg_s2", "direct", "pipelined"):
-                t = time_launches(launcher(tdg, w, da, db, c, variant), 20, 3)
+                t = time_launches(launcher(tdg, w, da, db, c, variant), 100, 20)
                 tp, bw = throughput(w, t)
                 row[variant] = {"us": round(t * 1e3, 2), "tops": round(tp, 1), "gbs": round(bw, 1)}
             row["speedup_pipelined_vs_single"] = round(row["single"]["us"] / row["pipelined"]["us"], 3)
