@@ -34,9 +34,13 @@
  * K == 0 writes zeros to C.
  * Any shape and alignment is accepted.  The fast path needs 16-byte aligned
  * A and B, lda and ldb whole multiples of 16 bytes and M, N, K whole multiples
- * of the tile; anything else runs the bounds-checked form of the same kernel,
- * which zero-fills out-of-range loads and masks stores ("Pipeline GPU
- * Kernel", Common Pitfalls: boundary handling with async copies).
+ * of the tile.  A ragged shape with the same alignment and with N and K whole
+ * multiples of 16 bytes (8 FP16 or 16 INT8 elements) keeps the direct-to-LDS
+ * copy: chunks outside A or B are fetched from a zero block and stores are
+ * masked.  Anything else runs the bounds-checked register-prefetch form of
+ * the same kernel, which zero-fills out-of-range loads element by element
+ * ("Pipeline GPU Kernel", Common Pitfalls: boundary handling with async
+ * copies).
  * Errors: TDG_ERR_NO_DEVICE when the current device is not gfx950 or no
  * device is present; TDG_ERR_UNSUPPORTED for an explicit configuration that is
  * not built in or does not fit the device; TDG_ERR_LAUNCH when the launch

@@ -144,6 +144,18 @@ def test_planner_choices():
     assert cfg["bn"] == 64 and cfg["lds_stages"] >= 2 and info["grid"] >= 256
     cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_I8I32, 300, 290, 333)
     assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH
+    # ragged, but N and K whole 16-byte chunks: the copy stays in the DMA
+    for code, M, N, K in [(0, 300, 264, 200), (0, 4000, 4000, 4000), (1, 300, 272, 144),
+                          (0, 16383, 64, 8192), (1, 1, 16, 16)]:
+        cfg, info = tdg.tdg_plan(code, M, N, K)
+        assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS, (M, N, K)
+    # a K or N that splits a 16-byte chunk keeps the element-wise guarded loads
+    for code, M, N, K in [(0, 300, 264, 201), (0, 300, 260, 200), (1, 300, 272, 136)]:
+        cfg, info = tdg.tdg_plan(code, M, N, K)
+        assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH, (M, N, K)
+    # the 4000^3 plan keeps the 256x256 tile of the 4096^3 one
+    cfg, _ = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4000, 4000, 4000)
+    assert (cfg["bm"], cfg["bn"]) == (256, 256)
     # every built configuration can be planned back exactly
     for code in (0, 1):
         for i in range(tdg.tdg_config_count(code)):

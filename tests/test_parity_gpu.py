@@ -151,6 +151,62 @@ def test_ragged_every_tile(lib, dtype):
             _check(dtype, gemm(lib, dtype, "ex", dA, dB, cfg=cfg), A, B)
 
 
+# --- ragged shapes on the bounds-checked direct-to-LDS path --------------------------
+# N and K whole 16-byte chunks (8 FP16 / 16 INT8 elements), aligned rows: chunks
+# outside A or B come from a zero block, so the result must equal the one of the
+# element-wise guarded loop at the same tile bit for bit.
+
+RAGGED_DMA = [(1, 16, 16), (5, 32, 48), (300, 272, 144), (257, 144, 272), (130, 400, 528),
+              (1000, 16, 1040), (64, 64, 16)]
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("M,N,K", RAGGED_DMA)
+def test_ragged_direct_shapes(lib, dtype, M, N, K):
+    import torch
+    A, B = _operands(dtype, M, N, K, seed=3 * M + N + K)
+    dA, dB = to_device(A), to_device(B)
+    code = 0 if dtype == F16 else 1
+    cfg, info = lib.tdg_plan(code, M, N, K)
+    assert info["guarded"] == 1 and cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    _check(dtype, C, A, B)
+    reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
+    assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_ragged_direct_every_tile(lib, dtype):
+    """Every tile and every ring depth asked for on a ragged, chunk-aligned
+    shape: all forms agree bit for bit and with the oracle."""
+    import torch
+    M, N, K = 301, 288, 272
+    A, B = _operands(dtype, M, N, K, seed=98)
+    dA, dB = to_device(A), to_device(B)
+    for tile in (_tiles(0) if dtype == F16 else _tiles(1)):
+        ref_out = None
+        for name, cfg in _variants(lib, dtype, tile):
+            C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+            if ref_out is None:
+                _check(dtype, C, A, B)
+                ref_out = C
+            else:
+                assert torch.equal(ref_out, C), "%s differs at tile %s" % (name, tile)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_ragged_direct_padded_rows(lib, dtype):
+    """Leading dimensions wider than the matrix (still 16-byte multiples)
+    on the ragged direct path: nothing past a row's K or N is used."""
+    M, N, K = 200, 144, 176
+    bigA, bigB = _operands(dtype, M + 2, N + 48, K + 32, seed=17)
+    A, B = bigA[1:1 + M, :K], bigB[1:1 + K, 16:16 + N]
+    dA = to_device(bigA)[1:1 + M, :K]
+    dB = to_device(bigB)[1:1 + K, 16:16 + N]
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    _check(dtype, C, A, B)
+
+
 @pytest.mark.parametrize("dtype", [F16, I8])
 def test_k_zero_writes_zeros(lib, dtype):
     import torch
@@ -328,4 +384,25 @@ def test_full_size_sampled(lib, name):
     for vname, cfg in _variants(lib, dtype, tile):
         assert torch.equal(C_pipe, gemm(lib, dtype, "ex", dA, dB, cfg=cfg)), vname
     del C_pipe, C_single, dA, dB
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [(F16, 4000, 4000, 4000), (I8, 4000, 4000, 4000),
+                                         (F16, 16383, 64, 8184)])
+def test_large_ragged_sampled(lib, dtype, M, N, K):
+    """Ragged shapes near the benchmark sizes run the bounds-checked
+    direct-to-LDS loop; sampled elements (tile edges included) against the
+    oracle, and the whole output against the element-wise guarded loop."""
+    import torch
+    A, B = _operands(dtype, M, N, K, seed=M + K)
+    dA, dB = to_device(A), to_device(B)
+    code = 0 if dtype == F16 else 1
+    cfg, info = lib.tdg_plan(code, M, N, K)
+    assert info["guarded"] == 1 and cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS
+    rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=min(cfg["bn"], N))
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    check_sampled(C, dtype, A, B, rows, cols)
+    reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
+    assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
+    del C, dA, dB
     torch.cuda.empty_cache()

@@ -102,6 +102,15 @@ bool fast_ok(const KernelEntry &e, int64_t M, int64_t N, int64_t K, bool vec_ok)
     return vec_ok;
 }
 
+// Whether the bounds-checked direct-to-LDS loop may run on a ragged shape:
+// every 16-byte chunk of a row is either wholly inside the matrix or wholly
+// outside it (K and N whole chunks, aligned rows), so out-of-range chunks can
+// be fetched from a zero block and no DMA reads past an operand.
+bool edge_ok(const KernelEntry &e, int64_t N, int64_t K, bool vec_ok) {
+    const int epc = 16 / elem_size(e.dtype);
+    return vec_ok && K > 0 && K % epc == 0 && N % epc == 0;
+}
+
 bool aligned_operands(int dtype, const void *A, int64_t lda, const void *B, int64_t ldb) {
     const int es = elem_size(dtype);
     return ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((lda * es) % 16 == 0) &&
@@ -229,10 +238,11 @@ const KernelEntry *find_entry(const KernelEntry &tile, int stages, int variant, 
 }
 
 // Ring depth the direct-to-LDS loop uses when the caller leaves it open: the
-// measured best for the tile shape when there is one, else two buffers.
-int preferred_direct_stages(const KernelEntry &tile) {
+// measured best for the tile shape when it is built (in the plain or the
+// bounds-checked form, as asked), else two buffers.
+int preferred_direct_stages(const KernelEntry &tile, bool guard) {
     const Measured *m = measured_for(tile.bm, tile.bn, tile.bkb);
-    if (m && m->waves == cfg_waves(tile) && find_entry(tile, m->stages, TDG_VARIANT_DIRECT_LDS, false))
+    if (m && m->waves == cfg_waves(tile) && find_entry(tile, m->stages, TDG_VARIANT_DIRECT_LDS, guard))
         return m->stages;
     return 2;
 }
@@ -254,16 +264,18 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     if (!tile) return TDG_ERR_UNSUPPORTED;
     const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
     const bool fast = fast_ok(*tile, M, N, K, vec_ok);
+    const bool edge = !fast && edge_ok(*tile, N, K, vec_ok);
 
     int variant = req.variant;
     if (variant == TDG_VARIANT_AUTO)
-        variant = pipelined_default ? (fast ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
-                                    : TDG_VARIANT_SINGLE;
+        variant = pipelined_default
+                      ? (fast || edge ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
+                      : TDG_VARIANT_SINGLE;
     int stages = req.lds_stages;
     if (stages == 0)
         stages = variant == TDG_VARIANT_SINGLE ? 1
                  : variant == TDG_VARIANT_REG_PREFETCH ? 2
-                                                       : preferred_direct_stages(*tile);
+                                                       : preferred_direct_stages(*tile, !fast);
     if (variant == TDG_VARIANT_SINGLE && stages != 1) return TDG_ERR_UNSUPPORTED;
     if (variant == TDG_VARIANT_REG_PREFETCH && stages > 2) return TDG_ERR_UNSUPPORTED;
     if (variant == TDG_VARIANT_DIRECT_LDS && stages < 2) return TDG_ERR_UNSUPPORTED;
@@ -273,12 +285,28 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     if (!guard) {
         e = find_entry(*tile, stages, variant, false);
     } else if (variant == TDG_VARIANT_DIRECT_LDS) {
-        // The DMA needs valid, aligned sources for every 16-byte chunk; ragged
-        // or misaligned operands run the bounds-checked register-prefetch
-        // loop instead ("Pipeline GPU Kernel", Common Pitfalls).
-        variant = TDG_VARIANT_REG_PREFETCH;
-        e = find_entry(*tile, 2, variant, true);
-        stages = 2;
+        // The DMA needs valid, aligned sources for every 16-byte chunk
+        // ("Pipeline GPU Kernel", Common Pitfalls).  Ragged shapes whose rows
+        // are aligned whole chunks keep the copy in the DMA (bounds-checked
+        // form, at the asked ring depth if built, else the tile's preferred
+        // one, else two buffers); anything else runs the bounds-checked
+        // register-prefetch loop.
+        if (edge) {
+            e = find_entry(*tile, stages, variant, true);
+            if (!e) {
+                stages = preferred_direct_stages(*tile, true);
+                e = find_entry(*tile, stages, variant, true);
+            }
+            if (!e) {
+                stages = 2;
+                e = find_entry(*tile, stages, variant, true);
+            }
+        }
+        if (!e) {
+            variant = TDG_VARIANT_REG_PREFETCH;
+            e = find_entry(*tile, 2, variant, true);
+            stages = 2;
+        }
     } else if (variant == TDG_VARIANT_REG_PREFETCH && stages == 1) {
         e = find_entry(*tile, 2, variant, true);
         stages = 2;

@@ -1,10 +1,11 @@
 // tdg_kernels.hip -- the built-in kernel configurations and their table.
 //
 // Each tile shape (BM x BN, K tile of BKB bytes, WM x WN waves) is built for
-// both dtypes in six forms: the sequential baseline, the register-prefetch
+// both dtypes in seven forms: the sequential baseline, the register-prefetch
 // loop with one and with two LDS buffers, the direct-to-LDS loop, and the
-// bounds-checked forms of the baseline and of the double-buffered
-// register-prefetch loop (used for ragged or misaligned operands).
+// bounds-checked forms of the baseline, of the double-buffered
+// register-prefetch loop (any ragged or misaligned operands) and of the
+// direct-to-LDS loop (ragged shapes with aligned, whole-chunk rows).
 #include "tdg_internal.h"
 #include "tdg_kernels.hpp"
 
@@ -21,10 +22,13 @@ namespace tdg {
         TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_REG, false),              \
         TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_DIRECT, false),           \
         TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 1, VAR_SINGLE, true),            \
-        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_REG, true)
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_REG, true),               \
+        TDG_ENTRY(DT, BM, BN, BKB, WM, WN, 2, VAR_DIRECT, true)
 
 // Deeper direct-to-LDS rings where the LDS budget allows.
 #define TDG_DIRECT(DT, BM, BN, BKB, WM, WN, ST) TDG_ENTRY(DT, BM, BN, BKB, WM, WN, ST, VAR_DIRECT, false)
+// ... and their bounds-checked forms for the rings the planner picks.
+#define TDG_DIRECT_G(DT, BM, BN, BKB, WM, WN, ST) TDG_ENTRY(DT, BM, BN, BKB, WM, WN, ST, VAR_DIRECT, true)
 
 #define TDG_SHAPES(DT)                                                                   \
     TDG_SHAPE(DT, 256, 256, 128, 2, 2), TDG_SHAPE(DT, 256, 256, 128, 2, 4),              \
@@ -35,8 +39,9 @@ namespace tdg {
         TDG_SHAPE(DT, 128, 128, 128, 2, 2), TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3),      \
         TDG_DIRECT(DT, 128, 128, 128, 2, 2, 4), TDG_SHAPE(DT, 128, 64, 128, 4, 1),       \
         TDG_DIRECT(DT, 128, 64, 128, 4, 1, 4), TDG_DIRECT(DT, 128, 64, 128, 4, 1, 6),    \
-        TDG_SHAPE(DT, 64, 64, 128, 2, 2), TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4),          \
-        TDG_DIRECT(DT, 64, 64, 128, 2, 2, 8)
+        TDG_DIRECT_G(DT, 128, 64, 128, 4, 1, 4), TDG_SHAPE(DT, 64, 64, 128, 2, 2),       \
+        TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4), TDG_DIRECT(DT, 64, 64, 128, 2, 2, 8),      \
+        TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 4)
 
 // Each dtype's table is its own translation unit (TDG_BUILD_DT = 0 or 1), so
 // the two halves compile in parallel.

@@ -176,6 +176,11 @@ __device__ static __forceinline__ void wait_vmcnt_upto(int r) {
     }
 }
 
+// Sixteen zero bytes: the DMA source of every chunk that lies outside A or B
+// on the bounds-checked direct-to-LDS path, so that chunk lands in LDS as
+// zeros while every lane still issues the same DMA instruction.
+static __device__ __attribute__((aligned(16))) const uint32_t tdg_zero16[4] = {0u, 0u, 0u, 0u};
+
 // Workgroup -> C tile.  Workgroups are dealt round-robin to the 8 XCDs, so
 // when the tile count is a multiple of 8, workgroup b is renumbered so that
 // each XCD receives a contiguous run of tile ids; the ids are then laid out in
@@ -224,8 +229,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     typedef typename MM::out_t out_t;
     static_assert(STAGES >= 1 && STAGES <= 8, "one to eight LDS buffers");
     static_assert(VAR == VAR_DIRECT || STAGES <= 2, "register staging holds one tile");
-    static_assert(VAR != VAR_DIRECT || (STAGES >= 2 && !GUARD),
-                  "direct-to-LDS runs on the aligned fast path with two or more buffers");
+    static_assert(VAR != VAR_DIRECT || STAGES >= 2, "direct-to-LDS needs two or more buffers");
     static_assert(STAGES * G::STAGE_BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
     static_assert(VAR != VAR_SINGLE || STAGES == 1, "the sequential baseline has one buffer");
 
@@ -341,8 +345,39 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // inline assembly so that the compiler does not guard the other buffer's
     // LDS reads with a wait on these copies; completion is awaited
     // explicitly (vmcnt) before the barrier that publishes the tile.
+    // Bounds-checked DMA (GUARD): the operands are 16-byte aligned with K and
+    // N whole 16-byte chunks, so a chunk is either wholly inside its matrix or
+    // wholly outside; one outside (A row >= M, k >= K; B row k >= K, column
+    // >= N) is fetched from the zero block instead.  The source is then a
+    // per-lane 64-bit address.  B columns >= N and A rows >= M only feed C
+    // elements that are never stored; k >= K must be zero.
+    constexpr int EPC = 16 / G::ES;
+    uint32_t a_rows_ok = 0;
+    if constexpr (GUARD) {
+#pragma unroll
+        for (int i = 0; i < G::CA; i++)
+            if (m0 + i * A_RSTEP + a_r0 < args.M) a_rows_ok |= 1u << i;
+    }
+    const bool b_col_ok = n0 + b_c * EPC < args.N;
+    const int a_kc = a_c * EPC;  // first k of this thread's A chunk within a tile
     auto issue_direct_one = [&](uint32_t st_off, int kt, int d) {
         const uint32_t wbase = smem_addr + st_off + (uint32_t)wave * 1024u;
+        if constexpr (GUARD) {
+            const unsigned char *src;
+            uint32_t m0v;
+            if (d < G::CA) {
+                const bool ok = ((a_rows_ok >> d) & 1u) && kt * G::BK + a_kc < args.K;
+                src = ok ? a_ptr(kt, d) + a_voff : (const unsigned char *)tdg_zero16;
+                m0v = wbase + (uint32_t)(d * G::NT * 16);
+            } else {
+                const int i = d - G::CA;
+                const bool ok = b_col_ok && kt * G::BK + i * B_RSTEP + b_k0 < args.K;
+                src = ok ? b_ptr(kt, i) + b_voff : (const unsigned char *)tdg_zero16;
+                m0v = wbase + (uint32_t)(G::A_BYTES + i * G::NT * 16);
+            }
+            asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0v) : "memory");
+            return;
+        }
         if (d < G::CA) {
             const uint32_t m0v = wbase + (uint32_t)(d * G::NT * 16);
             asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(a_voff), "s"(a_ptr(kt, d)),
