@@ -5,8 +5,9 @@ leg of the benchmark are the only callers.  The GPU library never imports,
 links or runs anything in this directory, and this directory never imports the
 GPU library.
 
-The arithmetic lives in ``oracle_gemm.c`` (plain C, built with gcc); this
-module only builds it and marshals numpy arrays into it.  What it computes is
+The arithmetic lives in ``oracle_gemm.c`` and ``oracle_move.c`` (plain C,
+built with gcc); this module only builds them and marshals numpy arrays into
+them.  What it computes is
 the textbook product, C[i][j] = sum_k A[i][k] * B[k][j] in increasing k, in
 int64 for INT8 inputs and in double for binary16 inputs (each input widened
 exactly), with S[i][j] = sum_k |A[i][k] * B[k][j]| beside the FP16 result.
@@ -28,15 +29,17 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle_gemm.c")
+_SRC_MOVE = os.path.join(_HERE, "oracle_move.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle_gemm.so")
 _lib = None
 
 
 def build() -> str:
-    """Compile oracle_gemm.c into liboracle_gemm.so with gcc (no fast-math)."""
+    """Compile oracle_gemm.c and oracle_move.c into liboracle_gemm.so with gcc
+    (no fast-math)."""
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-D_POSIX_C_SOURCE=200809L", "-fPIC", "-shared",
-           "-pthread", "-o", tmp, _SRC, "-lm"]
+           "-pthread", "-o", tmp, _SRC, _SRC_MOVE, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -46,7 +49,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_SRC_MOVE))
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         build()
     lib = ctypes.CDLL(_LIB_PATH)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
@@ -60,6 +64,9 @@ def _load():
     lib.oracle_gemm_i8i64_at.restype = ctypes.c_int
     lib.oracle_gemm_f16f64_at.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, vp, vp]
     lib.oracle_gemm_f16f64_at.restype = ctypes.c_int
+    for name in ("oracle_copy_u32", "oracle_transpose_u32"):
+        getattr(lib, name).argtypes = [i64, i64, vp, i64, vp, i64]
+        getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -171,3 +178,30 @@ def f16_to_f64(bits: np.ndarray) -> np.ndarray:
     flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
     return np.array([lib.oracle_f16_to_f64(int(h)) for h in flat], dtype=np.float64).reshape(
         np.shape(bits))
+
+
+def _u32_operand(x: np.ndarray):
+    """A 2-D array of 32-bit elements (float32 or uint32) as uint32 bits."""
+    if x.dtype == np.float32:
+        x = x.view(np.uint32)
+    return _operand(x, np.uint32)
+
+
+def copy_u32(x: np.ndarray) -> np.ndarray:
+    """out[i][j] = x[i][j] for a 2-D array of 32-bit elements (returns uint32
+    bits; "fixing GPU kernels by hand", the copy that bounds the transpose)."""
+    rows, cols, px, ldx = _u32_operand(x)
+    out = np.empty((rows, cols), dtype=np.uint32)
+    _check(_load().oracle_copy_u32(rows, cols, px, ldx, out.ctypes.data, max(1, cols)),
+           "oracle_copy_u32")
+    return out
+
+
+def transpose_u32(x: np.ndarray) -> np.ndarray:
+    """out[j][i] = x[i][j] for a 2-D array of 32-bit elements (returns uint32
+    bits; "fixing GPU kernels by hand", the transpose exercise)."""
+    rows, cols, px, ldx = _u32_operand(x)
+    out = np.empty((cols, rows), dtype=np.uint32)
+    _check(_load().oracle_transpose_u32(rows, cols, px, ldx, out.ctypes.data, max(1, rows)),
+           "oracle_transpose_u32")
+    return out
