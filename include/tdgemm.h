@@ -160,6 +160,44 @@ int tdg_config_at(int dtype, int index, tdg_config *out);
 /* Human-readable name of a status code (static storage). */
 const char *tdg_status_string(int status);
 
+/* ---- Copy / transpose ladder ("fixing GPU kernels by hand", the transpose
+ * exercise in four steps).  A rows x cols matrix of 32-bit elements (float;
+ * the bits are moved, never computed on) is copied or transposed between
+ * device buffers owned by the caller.  Effective bandwidth is the bytes that
+ * must move, 2 * rows * cols * 4, over the time.  The copy is the upper bound
+ * every transpose is measured against; the methods are the page's ladder on
+ * gfx950 (64-lane waves, 64 LDS banks), plus two MI355X steps:
+ *   NAIVE         coalesced reads, writes strided by the output row length;
+ *   LDS           through a 64 x 64 LDS tile read by columns (every column
+ *                 read is a 64-way bank conflict);
+ *   LDS_PADDED    the page's fix: one extra word per tile row;
+ *   LDS_SWIZZLED  the same without the extra word (column index XOR row);
+ *   VEC           16-byte loads and stores on both sides of a swizzled tile
+ *                 (whole tiles of 16-byte aligned operands; other tiles take
+ *                 the LDS_SWIZZLED path).
+ * AUTO is VEC.  Arguments: rows, cols >= 0 (and below 2^31 - 64);
+ * ldi >= max(1, cols); ldo >= max(1, cols) for the copy and >= max(1, rows)
+ * for the transpose (out is cols x rows); a pointer may be NULL only when the
+ * matrix is empty; out may not overlap in.  Violations return
+ * TDG_ERR_INVALID_ARG before any HIP call; an empty matrix returns TDG_OK
+ * with no launch; a non-gfx950 device returns TDG_ERR_NO_DEVICE; a failed
+ * launch TDG_ERR_LAUNCH.  Asynchronous on `stream`, like the GEMM calls. */
+typedef enum {
+    TDG_TRANSPOSE_AUTO = 0,
+    TDG_TRANSPOSE_NAIVE = 1,
+    TDG_TRANSPOSE_LDS = 2,
+    TDG_TRANSPOSE_LDS_PADDED = 3,
+    TDG_TRANSPOSE_LDS_SWIZZLED = 4,
+    TDG_TRANSPOSE_VEC = 5
+} tdg_transpose_method;
+
+/* out[i][j] = in[i][j]; out is rows x cols. */
+int tdg_copy_f32(int64_t rows, int64_t cols, const float *in, int64_t ldi, float *out,
+                 int64_t ldo, void *stream);
+/* out[j][i] = in[i][j]; out is cols x rows. */
+int tdg_transpose_f32(int method, int64_t rows, int64_t cols, const float *in, int64_t ldi,
+                      float *out, int64_t ldo, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,46 @@ def test_empty_output_returns_ok_without_a_device():
     assert tdg.call_raw("gemm_i8i32", 4, 0, 4, 4096, 4, 0, 1, 0, 1) == tdg.TDG_OK
 
 
+# --- copy / transpose ladder: the same validation rules -------------------------------
+
+def _move(name, *args):
+    lib = tdg.load_library()
+    return getattr(lib, name)(*args)
+
+
+MOVE_BAD = [
+    ("negative rows", (-1, 4, 4096, 4, 1 << 20, 4)),
+    ("ldi < cols", (4, 8, 4096, 4, 1 << 20, 8)),
+    ("NULL in", (4, 4, 0, 4, 1 << 20, 4)),
+    ("NULL out", (4, 4, 4096, 4, 0, 4)),
+    ("out overlaps in", (4, 4, 4096, 4, 4096 + 32, 4)),
+    ("rows too large", (1 << 31, 4, 4096, 4, 1 << 40, 4)),
+]
+
+
+@pytest.mark.parametrize("what,args", MOVE_BAD, ids=[b[0] for b in MOVE_BAD])
+def test_move_invalid_arguments(what, args):
+    assert _move("tdg_copy_f32", *args, None) == tdg.TDG_ERR_INVALID_ARG
+    for method in range(6):
+        assert _move("tdg_transpose_f32", method, *args, None) == tdg.TDG_ERR_INVALID_ARG
+
+
+def test_move_output_leading_dimension_rules():
+    # copy: ldo >= cols; transpose: out is cols x rows, so ldo >= rows
+    assert _move("tdg_copy_f32", 8, 16, 4096, 16, 1 << 20, 8, None) == tdg.TDG_ERR_INVALID_ARG
+    assert _move("tdg_transpose_f32", 0, 16, 8, 4096, 8, 1 << 20, 8, None) == \
+        tdg.TDG_ERR_INVALID_ARG
+    # an unknown method
+    assert _move("tdg_transpose_f32", 6, 4, 4, 4096, 4, 1 << 20, 4, None) == tdg.TDG_ERR_INVALID_ARG
+    assert _move("tdg_transpose_f32", -1, 4, 4, 4096, 4, 1 << 20, 4, None) == \
+        tdg.TDG_ERR_INVALID_ARG
+
+
+def test_move_empty_matrix_returns_ok_without_a_device():
+    assert _move("tdg_copy_f32", 0, 5, 0, 5, 0, 5, None) == tdg.TDG_OK
+    assert _move("tdg_transpose_f32", 3, 7, 0, 0, 1, 0, 7, None) == tdg.TDG_OK
+
+
 def test_unbuilt_configuration_is_unsupported():
     cfg = tdg.TdgConfig(bm=96, bn=96, bk=0, waves=0, lds_stages=0, variant=0)
     with pytest.raises(tdg.TdgError) as e:

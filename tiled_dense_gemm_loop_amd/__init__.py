@@ -1,8 +1,8 @@
 """MI355X (gfx950) software-pipelined tiled dense GEMM.
 
 C = A . B with FP16 inputs / FP32 accumulation and INT8 inputs / INT32
-accumulation, computed by hand-written HIP kernels behind the C ABI of
-include/tdgemm.h.  This package is the thin Python binding of that library
+accumulation, plus the copy / transpose ladder on HBM, computed by
+hand-written HIP kernels behind the C ABI of include/tdgemm.h.  This package is the thin Python binding of that library
 (argument marshalling only) plus its build script.
 """
 from ._binding import (  # noqa: F401
@@ -15,6 +15,13 @@ from ._binding import (  # noqa: F401
     TDG_ERR_NO_DEVICE,
     TDG_ERR_UNSUPPORTED,
     TDG_OK,
+    TDG_TRANSPOSE_AUTO,
+    TDG_TRANSPOSE_LDS,
+    TDG_TRANSPOSE_LDS_PADDED,
+    TDG_TRANSPOSE_LDS_SWIZZLED,
+    TDG_TRANSPOSE_NAIVE,
+    TDG_TRANSPOSE_VEC,
+    TRANSPOSE_NAMES,
     TDG_VARIANT_AUTO,
     TDG_VARIANT_DIRECT_LDS,
     TDG_VARIANT_REG_PREFETCH,
@@ -33,7 +40,9 @@ from ._binding import (  # noqa: F401
     load_library,
     tdg_config_at,
     tdg_config_count,
+    tdg_copy_f32,
     tdg_plan,
     tdg_status_string,
     tdg_tile_figures,
+    tdg_transpose_f32,
 )

@@ -29,11 +29,20 @@ TDG_VARIANT_DIRECT_LDS = 3
 
 VARIANT_NAMES = {0: "auto", 1: "single", 2: "reg_prefetch", 3: "direct_lds"}
 
+TDG_TRANSPOSE_AUTO = 0
+TDG_TRANSPOSE_NAIVE = 1
+TDG_TRANSPOSE_LDS = 2
+TDG_TRANSPOSE_LDS_PADDED = 3
+TDG_TRANSPOSE_LDS_SWIZZLED = 4
+TDG_TRANSPOSE_VEC = 5
+
+TRANSPOSE_NAMES = {1: "naive", 2: "lds", 3: "lds_padded", 4: "lds_swizzled", 5: "vec"}
+
 # Every symbol include/tdgemm.h declares.
 EXPORTED = (
     "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
     "gemm_f16f32_ex", "gemm_i8i32_ex", "tdg_plan", "tdg_tile_figures", "tdg_config_count",
-    "tdg_config_at", "tdg_status_string",
+    "tdg_config_at", "tdg_status_string", "tdg_copy_f32", "tdg_transpose_f32",
 )
 
 
@@ -103,6 +112,10 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_config_at.restype = c_int
     lib.tdg_status_string.argtypes = [c_int]
     lib.tdg_status_string.restype = ctypes.c_char_p
+    lib.tdg_copy_f32.argtypes = [i64, i64, vp, i64, vp, i64, vp]
+    lib.tdg_copy_f32.restype = c_int
+    lib.tdg_transpose_f32.argtypes = [c_int, i64, i64, vp, i64, vp, i64, vp]
+    lib.tdg_transpose_f32.restype = c_int
     _lib = lib
     return lib
 
@@ -241,3 +254,36 @@ def tdg_config_at(dtype: int, index: int) -> dict:
 
 def tdg_status_string(status: int) -> str:
     return status_string(status)
+
+
+# ------------------------------------------------------ copy / transpose ladder
+
+def _move(x, out, transpose, method):
+    torch = _torch()
+    rows, cols, px, ldi = _matrix(x, (torch.float32,), "in")
+    shape = (cols, rows) if transpose else (rows, cols)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    orow, ocol, po, ldo = _matrix(out, (torch.float32,), "out")
+    if (orow, ocol) != shape:
+        raise ValueError("out has shape %s, expected %s" % ((orow, ocol), shape))
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        if transpose:
+            rc = lib.tdg_transpose_f32(int(method), rows, cols, px, ldi, po, ldo, stream)
+        else:
+            rc = lib.tdg_copy_f32(rows, cols, px, ldi, po, ldo, stream)
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_transpose_f32" if transpose else "tdg_copy_f32")
+    return out
+
+
+def tdg_copy_f32(x, out=None):
+    """out[i][j] = x[i][j] (float32, device tensors; rows may be strided)."""
+    return _move(x, out, False, 0)
+
+
+def tdg_transpose_f32(x, out=None, method=TDG_TRANSPOSE_AUTO):
+    """out[j][i] = x[i][j] with one of the ladder's methods."""
+    return _move(x, out, True, method)

@@ -32,11 +32,29 @@ const KernelEntry *kernel_table(int *count) {
     return all;
 }
 
+// Whether the current device is gfx950 (cached per device).
+static std::mutex g_dev_mutex;
+static signed char g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int device_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TDG_ERR_NO_DEVICE;
+    if (dev < 0 || dev >= 64) return TDG_ERR_NO_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TDG_ERR_NO_DEVICE;
+        g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return g_dev_ok[dev] == 1 ? TDG_OK : TDG_ERR_NO_DEVICE;
+}
+
 }  // namespace tdg
 
 namespace {
 
 using tdg::KernelEntry;
+using tdg::device_check;
 
 constexpr int kNumCU = 256;               // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;     // gfx950 LDS per CU
@@ -332,27 +350,6 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         cfg_out->variant = variant;
     }
     fill_info(*e, variant, stages, M, N, K, guard, info);
-    return TDG_OK;
-}
-
-// ------------------------------------------------------------------- device
-
-std::mutex g_dev_mutex;
-signed char g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
-
-int device_check() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return TDG_ERR_NO_DEVICE;
-    if (dev < 0 || dev >= 64) return TDG_ERR_NO_DEVICE;
-    {
-        std::lock_guard<std::mutex> lock(g_dev_mutex);
-        if (g_dev_ok[dev] == 0) {
-            hipDeviceProp_t prop;
-            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TDG_ERR_NO_DEVICE;
-            g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-        }
-        if (g_dev_ok[dev] != 1) return TDG_ERR_NO_DEVICE;
-    }
     return TDG_OK;
 }
 

@@ -22,4 +22,7 @@ const KernelEntry *kernel_table_f16(int *count);
 const KernelEntry *kernel_table_i8(int *count);
 const KernelEntry *kernel_table(int *count);
 
+// TDG_OK when the current device is gfx950, else TDG_ERR_NO_DEVICE.
+int device_check();
+
 }  // namespace tdg
