@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--no-table", action="store_true", help="skip the per-workload variant table")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--no-ladder", action="store_true", help="skip the copy/transpose ladder")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured MFMA ceilings (MFMA-only probe)")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -130,11 +133,72 @@ def time_launches(run, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
+def individual_launches(run, count: int = 50) -> dict:
+    """Median / min / max microseconds of `count` launches, each bracketed by
+    its own pair of events on the launching stream."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(count)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return {"count": count, "median_us": round(us[count // 2], 2), "min_us": round(us[0], 2),
+            "max_us": round(us[-1], 2)}
+
+
 def throughput(wl, ms: float):
     ops = 2.0 * wl.M * wl.N * wl.K
     es = 2 if wl.dtype == "f16" else 1
     alg_bytes = (wl.M * wl.K + wl.K * wl.N) * es + wl.M * wl.N * 4
     return ops / (ms * 1e-3) / 1e12, alg_bytes / (ms * 1e-3) / 1e9
+
+
+def transpose_ladder(tdg):
+    """The copy / transpose ladder ("fixing GPU kernels by hand"): effective
+    bandwidth = 2 * n^2 * 4 bytes over the mean launch time, for the page's
+    4096^2 float matrix (input and output fit the 256 MB last-level cache)
+    and for 16384^2 (1 GiB each way, HBM-bound)."""
+    import torch
+    out = {}
+    for n, steps in ((4096, 200), (16384, 40)):
+        x = torch.randn(n, n, device="cuda")
+        y = torch.empty(n, n, device="cuda")
+        moved = 2.0 * n * n * 4
+        rows = {"copy": time_launches(lambda: tdg.tdg_copy_f32(x, y), steps, 20)}
+        for code, name in tdg.TRANSPOSE_NAMES.items():
+            rows[name] = time_launches(lambda: tdg.tdg_transpose_f32(x, y, method=code), steps, 20)
+        copy_ms = rows["copy"]
+        out["%dx%d" % (n, n)] = {
+            name: {"us": round(ms * 1e3, 2), "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+                   "of_copy": round(copy_ms / ms, 3),
+                   "of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+            for name, ms in rows.items()}
+        print("# ladder %dx%d %s" % (n, n, json.dumps(out["%dx%d" % (n, n)])), file=sys.stderr,
+              flush=True)
+        del x, y
+        torch.cuda.empty_cache()
+    return out
+
+
+def measured_ceilings(tdg, ladder):
+    """Second denominators: the MFMA rate the chip sustains with no memory
+    traffic (tdg_mfma_probe, ~50 ms per launch so the power controller
+    settles) and the bandwidth of the library's copy on a matrix far larger
+    than the last-level cache."""
+    import torch
+    out = {}
+    sink = torch.empty(tdg.tdg_mfma_probe_sink_floats(), dtype=torch.float32, device="cuda")
+    for code, key, iters in ((tdg.TDG_DTYPE_F16F32, "mfma_f16_tflops", 200),
+                             (tdg.TDG_DTYPE_I8I32, "mfma_i8_tops", 100)):
+        ms = time_launches(lambda: tdg.tdg_mfma_probe(code, iters, sink), 4, 1)
+        out[key] = round(tdg.tdg_mfma_probe_ops(code, iters) / (ms * 1e-3) / 1e12, 1)
+    if ladder and "16384x16384" in ladder:
+        out["copy_gbs"] = ladder["16384x16384"]["copy"]["gbs"]
+    print("# measured ceilings %s" % json.dumps(out), file=sys.stderr, flush=True)
+    return out
 
 
 def cpu_baseline(wl, A, B, target_s: float):
@@ -176,6 +240,7 @@ def main():
     run = launcher(tdg, wl, dA, dB, C, "pipelined")
     ms = time_launches(run, args.steps, args.warmup)
     tops, gbs = throughput(wl, ms)
+    launches = individual_launches(run)
     dcode = tdg.TDG_DTYPE_F16F32 if wl.dtype == "f16" else tdg.TDG_DTYPE_I8I32
     cfg, info = tdg.tdg_plan(dcode, wl.M, wl.N, wl.K)
     unit = "TFLOP/s" if wl.dtype == "f16" else "TOP/s"
@@ -202,6 +267,9 @@ def main():
                 del a, b, da, db, c
                 torch.cuda.empty_cache()
 
+    ladder = None if args.no_ladder else transpose_ladder(tdg)
+    ceilings = {} if args.no_ceilings else measured_ceilings(tdg, ladder)
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -217,10 +285,22 @@ def main():
         cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
         tdg.VARIANT_NAMES[cfg["variant"]])
     traffic = profiled_traffic(kernel_desc)
+    es = 2 if wl.dtype == "f16" else 1
+    alg_bytes = (wl.M * wl.K + wl.K * wl.N) * es + wl.M * wl.N * 4
+    bound = roofline_bound(2.0 * wl.M * wl.N * wl.K, alg_bytes, PEAK[wl.dtype] * 1e3,
+                           HBM_PEAK_GBS)
+    if bound == "mfma":
+        achieved, peak, r_unit = round(tops, 2), PEAK[wl.dtype], unit
+        measured = ceilings.get("mfma_f16_tflops" if wl.dtype == "f16" else "mfma_i8_tops")
+    else:
+        achieved, peak, r_unit = round(gbs, 1), HBM_PEAK_GBS, "GB/s"
+        measured = ceilings.get("copy_gbs")
+    # the headline is the roofline's own quantity: operations per second for
+    # an MFMA-bound product, bytes per second for an HBM-bound one
     line = {
         "metric": METRIC,
-        "value": round(tops, 2),
-        "unit": unit,
+        "value": achieved,
+        "unit": r_unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -234,11 +314,15 @@ def main():
                    "accumulate": "f32" if wl.dtype == "f16" else "i32",
                    "kernel": kernel_desc,
                    "parallelism": "none"},
-        "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK[wl.dtype],
-                     "unit": unit, "frac": round(tops / PEAK[wl.dtype], 4),
-                     "traffic": traffic},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": r_unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "measured_peak": measured,
+                     "frac_of_measured": round(achieved / measured, 4) if measured else None},
+        "measured_ceilings": ceilings,
+        "launches": launches,
         "cpu_baseline": cpu,
         "variants": table or None,
+        "transpose_ladder": ladder,
     }
     print(json.dumps(line), flush=True)
 

@@ -172,9 +172,9 @@ const char *tdg_status_string(int status);
  *                 read is a 64-way bank conflict);
  *   LDS_PADDED    the page's fix: one extra word per tile row;
  *   LDS_SWIZZLED  the same without the extra word (column index XOR row);
- *   VEC           16-byte loads and stores on both sides of a swizzled tile
- *                 (whole tiles of 16-byte aligned operands; other tiles take
- *                 the LDS_SWIZZLED path).
+ *   VEC           16-byte loads and stores on both sides of a swizzled,
+ *                 pre-transposed tile (whole tiles of 16-byte aligned
+ *                 operands; other tiles take the LDS_SWIZZLED path).
  * AUTO is VEC.  Arguments: rows, cols >= 0 (and below 2^31 - 64);
  * ldi >= max(1, cols); ldo >= max(1, cols) for the copy and >= max(1, rows)
  * for the transpose (out is cols x rows); a pointer may be NULL only when the
@@ -197,6 +197,22 @@ int tdg_copy_f32(int64_t rows, int64_t cols, const float *in, int64_t ldi, float
 /* out[j][i] = in[i][j]; out is cols x rows. */
 int tdg_transpose_f32(int method, int64_t rows, int64_t cols, const float *in, int64_t ldi,
                       float *out, int64_t ldo, void *stream);
+
+/* ---- Measured compute ceiling ("Analyze Kernel Bottleneck", Step 2: set
+ * achieved throughput against what the hardware sustains).  Launches a kernel
+ * that issues only the GEMM's MFMA instruction (v_mfma_f32_32x32x16_f16 or
+ * v_mfma_i32_32x32x32_i8) with changing pseudo-random operands and no memory
+ * traffic: 512 workgroups of 4 waves (two waves per SIMD on 256 CUs), each
+ * wave `iters` x 8 MFMAs on eight independent accumulators.  iters must be a
+ * non-negative multiple of 4.  `sink` is a device buffer of
+ * tdg_mfma_probe_sink_floats() floats the kernel writes (so the work is not
+ * optimised away).  Returns TDG_ERR_INVALID_ARG for a bad dtype, iters or a
+ * NULL sink; TDG_ERR_NO_DEVICE off gfx950.  tdg_mfma_probe_ops gives the
+ * operations one launch performs (2 * 32 * 32 * k per MFMA), or -1 for bad
+ * arguments; time a launch and divide. */
+int tdg_mfma_probe(int dtype, int64_t iters, float *sink, void *stream);
+int64_t tdg_mfma_probe_ops(int dtype, int64_t iters);
+int64_t tdg_mfma_probe_sink_floats(void);
 
 #ifdef __cplusplus
 }

@@ -81,4 +81,7 @@ WORKLOADS = {
     "int8_4096": _wl(3, "int8_4096", "i8", 4096, 4096, 4096, "uniform_i8"),
     "fp16_4096": _wl(4, "fp16_4096", "f16", 4096, 4096, 4096, "normal"),
     "fp16_skinny": _wl(5, "fp16_skinny", "f16", 16384, 64, 8192, "uniform_pm1"),
+    # a ragged neighbour of the 4096^3 workload: no dimension a tile multiple,
+    # N and K whole 16-byte chunks (the bounds-checked direct-to-LDS loop)
+    "fp16_ragged": _wl(6, "fp16_ragged", "f16", 4000, 4000, 4000, "normal"),
 }

@@ -107,6 +107,18 @@ def test_move_empty_matrix_returns_ok_without_a_device():
     assert _move("tdg_transpose_f32", 3, 7, 0, 0, 1, 0, 7, None) == tdg.TDG_OK
 
 
+def test_mfma_probe_arguments():
+    lib = tdg.load_library()
+    assert lib.tdg_mfma_probe(7, 4, 4096, None) == tdg.TDG_ERR_INVALID_ARG
+    assert lib.tdg_mfma_probe(0, 3, 4096, None) == tdg.TDG_ERR_INVALID_ARG
+    assert lib.tdg_mfma_probe(0, 4, None, None) == tdg.TDG_ERR_INVALID_ARG
+    assert tdg.tdg_mfma_probe_ops(0, 3) == -1 and tdg.tdg_mfma_probe_ops(2, 4) == -1
+    # 512 workgroups x 4 waves x 8 MFMAs per step; 2*32*32*k operations each
+    assert tdg.tdg_mfma_probe_ops(0, 4) == 2 * 32 * 32 * 16 * 8 * 4 * 2048
+    assert tdg.tdg_mfma_probe_ops(1, 4) == 2 * tdg.tdg_mfma_probe_ops(0, 4)
+    assert tdg.tdg_mfma_probe_sink_floats() == 512 * 256
+
+
 def test_unbuilt_configuration_is_unsupported():
     cfg = tdg.TdgConfig(bm=96, bn=96, bk=0, waves=0, lds_stages=0, variant=0)
     with pytest.raises(tdg.TdgError) as e:

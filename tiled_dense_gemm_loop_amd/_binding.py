@@ -43,6 +43,7 @@ EXPORTED = (
     "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
     "gemm_f16f32_ex", "gemm_i8i32_ex", "tdg_plan", "tdg_tile_figures", "tdg_config_count",
     "tdg_config_at", "tdg_status_string", "tdg_copy_f32", "tdg_transpose_f32",
+    "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
 )
 
 
@@ -116,6 +117,12 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_copy_f32.restype = c_int
     lib.tdg_transpose_f32.argtypes = [c_int, i64, i64, vp, i64, vp, i64, vp]
     lib.tdg_transpose_f32.restype = c_int
+    lib.tdg_mfma_probe.argtypes = [c_int, i64, vp, vp]
+    lib.tdg_mfma_probe.restype = c_int
+    lib.tdg_mfma_probe_ops.argtypes = [c_int, i64]
+    lib.tdg_mfma_probe_ops.restype = i64
+    lib.tdg_mfma_probe_sink_floats.argtypes = []
+    lib.tdg_mfma_probe_sink_floats.restype = i64
     _lib = lib
     return lib
 
@@ -287,3 +294,32 @@ def tdg_copy_f32(x, out=None):
 def tdg_transpose_f32(x, out=None, method=TDG_TRANSPOSE_AUTO):
     """out[j][i] = x[i][j] with one of the ladder's methods."""
     return _move(x, out, True, method)
+
+
+# ------------------------------------------------------ measured compute ceiling
+
+def tdg_mfma_probe_ops(dtype: int, iters: int) -> int:
+    """Operations one tdg_mfma_probe launch performs."""
+    return load_library().tdg_mfma_probe_ops(dtype, iters)
+
+
+def tdg_mfma_probe_sink_floats() -> int:
+    return load_library().tdg_mfma_probe_sink_floats()
+
+
+def tdg_mfma_probe(dtype: int, iters: int, sink=None):
+    """Launch the MFMA-only kernel on the current stream; returns the sink
+    tensor (allocated when not given)."""
+    torch = _torch()
+    n = tdg_mfma_probe_sink_floats()
+    if sink is None:
+        sink = torch.empty(n, dtype=torch.float32, device="cuda")
+    if sink.dtype != torch.float32 or sink.numel() < n or not sink.is_cuda:
+        raise ValueError("sink must be a device float32 tensor of at least %d elements" % n)
+    lib = load_library()
+    with torch.cuda.device(sink.device):
+        stream = torch.cuda.current_stream(sink.device).cuda_stream
+        rc = lib.tdg_mfma_probe(dtype, iters, sink.data_ptr(), stream)
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_mfma_probe")
+    return sink

@@ -30,6 +30,7 @@ UNITS = [
     ("tdg_kernels.hip", ["-DTDG_BUILD_DT=1"], "tdg_kernels_i8.o"),
     ("tdg_api.hip", [], "tdg_api.o"),
     ("tdg_move.hip", [], "tdg_move.o"),
+    ("tdg_probe.hip", [], "tdg_probe.o"),
 ]
 
 

@@ -18,8 +18,10 @@
 //   VEC           gfx950's form: 16-byte loads and stores on both sides of
 //                 the tile (a lane moves four elements per access); the tile
 //                 is stored already transposed with a 4-word XOR swizzle, so
-//                 the scalar writes and the 16-byte reads of LDS are both
-//                 conflict-free.
+//                 the 16-byte LDS reads are conflict-free.
+// The copy marks its global accesses non-temporal: nothing is read twice, and
+// on a 1 GiB copy that measured 4-7% more bandwidth.  (The same hint made
+// VEC slower, at both sizes measured, so VEC keeps ordinary accesses.)
 // Tiles are 64 x 64 elements, one workgroup of 256 threads (4 waves) each.
 // Partial tiles at the matrix edges take element-wise, bounds-checked paths;
 // VEC runs its vector path on whole tiles of 16-byte aligned operands and
@@ -74,10 +76,12 @@ __global__ void __launch_bounds__(THREADS) k_copy(MoveArgs a) {
         u32x4 v[TILE / VEC_ROWS_PER_PASS];
 #pragma unroll
         for (int i = 0; i < TILE / VEC_ROWS_PER_PASS; i++)
-            v[i] = *(const u32x4 *)(in + (int64_t)(r0 + r + i * VEC_ROWS_PER_PASS) * a.ldi + c0 + 4 * q);
+            v[i] = __builtin_nontemporal_load(
+                (const u32x4 *)(in + (int64_t)(r0 + r + i * VEC_ROWS_PER_PASS) * a.ldi + c0 + 4 * q));
 #pragma unroll
         for (int i = 0; i < TILE / VEC_ROWS_PER_PASS; i++)
-            *(u32x4 *)(out + (int64_t)(r0 + r + i * VEC_ROWS_PER_PASS) * a.ldo + c0 + 4 * q) = v[i];
+            __builtin_nontemporal_store(
+                v[i], (u32x4 *)(out + (int64_t)(r0 + r + i * VEC_ROWS_PER_PASS) * a.ldo + c0 + 4 * q));
         return;
     }
     const int lane = tid & 63, wave = tid >> 6;
@@ -178,9 +182,14 @@ __global__ void __launch_bounds__(THREADS) k_transpose_lds(MoveArgs a) {
 
 // The tile is stored transposed: word (x, y) = input element (row y, column
 // x), at x * 64 + (y ^ (x & 60)).  The XOR term is a multiple of 4, so each
-// group of four consecutive y stays one aligned 16-byte chunk; it spreads the
-// 16 rows x that one wave-wide scalar store touches over 16 distinct chunks
-// of the bank line.
+// group of four consecutive y stays one aligned 16-byte chunk, and the 16
+// lanes that read one x back get 16 distinct chunks: the 16-byte reads are
+// conflict-free (measured).  Each wave-wide scalar store touches 16 rows x
+// at 64 distinct banks; gfx950 still charges such a store about two
+// conflict cycles (measured: its 4-byte stores run conflict-free when each
+// 16-lane group writes one contiguous 64-byte run, not when a group's words
+// are spread over a row and the rows change between groups).  The store
+// side costs no bandwidth here: the transpose is HBM-bound.
 __device__ __forceinline__ int vec_at(int x, int y) { return x * TILE + (y ^ (x & 60)); }
 
 __global__ void __launch_bounds__(THREADS) k_transpose_vec(MoveArgs a) {
