@@ -9,8 +9,9 @@ The arithmetic lives in ``oracle_gemm.c`` and ``oracle_move.c`` (plain C,
 built with gcc); this module only builds them and marshals numpy arrays into
 them.  What it computes is
 the textbook product, C[i][j] = sum_k A[i][k] * B[k][j] in increasing k, in
-int64 for INT8 inputs and in double for binary16 inputs (each input widened
-exactly), with S[i][j] = sum_k |A[i][k] * B[k][j]| beside the FP16 result.
+int64 for INT8 inputs and in double for binary16 and binary32 inputs (each
+input widened exactly), with S[i][j] = sum_k |A[i][k] * B[k][j]| beside the
+floating-point results.
 ("Pipeline GPU Kernel", Step 2 and Step 5; "Analyze Kernel Bottleneck",
 Step 1.)
 
@@ -64,6 +65,10 @@ def _load():
     lib.oracle_gemm_i8i64_at.restype = ctypes.c_int
     lib.oracle_gemm_f16f64_at.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, vp, vp]
     lib.oracle_gemm_f16f64_at.restype = ctypes.c_int
+    lib.oracle_gemm_f32f64.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, ctypes.c_int]
+    lib.oracle_gemm_f32f64.restype = ctypes.c_int
+    lib.oracle_gemm_f32f64_at.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64, vp, vp]
+    lib.oracle_gemm_f32f64_at.restype = ctypes.c_int
     for name in ("oracle_copy_u32", "oracle_transpose_u32"):
         getattr(lib, name).argtypes = [i64, i64, vp, i64, vp, i64]
         getattr(lib, name).restype = ctypes.c_int
@@ -133,6 +138,22 @@ def gemm_f16(A: np.ndarray, B: np.ndarray, threads: int | None = None,
     return C, S
 
 
+def gemm_f32(A: np.ndarray, B: np.ndarray, threads: int | None = None,
+             with_scale: bool = True):
+    """C = A.B for binary32 A (M x K) and B (K x N); returns (C, S) as float64
+    arrays, S = sum_k |a_ik b_kj| (None when with_scale is False)."""
+    M, K, pa, lda = _operand(A, np.float32)
+    K2, N, pb, ldb = _operand(B, np.float32)
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    C = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64) if with_scale else None
+    _check(_load().oracle_gemm_f32f64(M, N, K, pa, lda, pb, ldb, C.ctypes.data,
+                                      S.ctypes.data if S is not None else None,
+                                      threads or host_threads()), "oracle_gemm_f32f64")
+    return C, S
+
+
 def _index_arrays(rows, cols):
     r = np.ascontiguousarray(rows, dtype=np.int64)
     c = np.ascontiguousarray(cols, dtype=np.int64)
@@ -169,6 +190,21 @@ def gemm_f16_at(A: np.ndarray, B: np.ndarray, rows, cols):
     _check(_load().oracle_gemm_f16f64_at(M, N, K, pa, lda, pb, ldb, r.ctypes.data,
                                          c.ctypes.data, r.size, out.ctypes.data,
                                          out_s.ctypes.data), "oracle_gemm_f16f64_at")
+    return out, out_s
+
+
+def gemm_f32_at(A: np.ndarray, B: np.ndarray, rows, cols):
+    """The elements (C, S)[rows[t], cols[t]] of C = A.B (binary32 inputs)."""
+    M, K, pa, lda = _operand(A, np.float32)
+    K2, N, pb, ldb = _operand(B, np.float32)
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    r, c = _index_arrays(rows, cols)
+    out = np.empty(r.shape, dtype=np.float64)
+    out_s = np.empty(r.shape, dtype=np.float64)
+    _check(_load().oracle_gemm_f32f64_at(M, N, K, pa, lda, pb, ldb, r.ctypes.data,
+                                         c.ctypes.data, r.size, out.ctypes.data,
+                                         out_s.ctypes.data), "oracle_gemm_f32f64_at")
     return out, out_s
 
 

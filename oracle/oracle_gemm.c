@@ -25,6 +25,11 @@
  *     double in increasing k.  Alongside it the oracle returns
  *     S[i][j] = sum_k |A[i][k]*B[k][j]|, the scale of the per-element error
  *     bound |C_gpu - C| <= 1e-4 * S.
+ *   - FP32 inputs ("Pipeline GPU Kernel", Step 5 lists FP32 scalar FFMA as
+ *     the third data type): each binary32 value converts to double exactly,
+ *     every product of two binary32 values (48 significant bits at most) is
+ *     exact in double, the sum runs in double in increasing k, and S is
+ *     returned alongside as for FP16.
  *
  * Parallelism: rows of C are split into contiguous bands, one per thread.
  * Each C[i][j] is still one sequential sum in increasing k, so the thread
@@ -71,7 +76,7 @@ static void f16_table_fill(void)
 }
 
 typedef struct {
-    int kind; /* 0: int8 -> int64, 1: fp16 -> double (+ S) */
+    int kind; /* 0: int8 -> int64, 1: fp16 -> double (+ S), 2: fp32 -> double (+ S) */
     int64_t row_begin, row_end, N, K;
     const void *A;
     int64_t lda;
@@ -127,13 +132,43 @@ static void band_f16(const band_t *t)
     }
 }
 
+/* binary32 inputs: a float converts to double exactly, and the product of
+ * two binary32 values (at most 48 significant bits) is exact in double. */
+static void band_f32(const band_t *t)
+{
+    const float *A = (const float *)t->A;
+    const float *B = (const float *)t->B;
+    double *C = (double *)t->C;
+    for (int64_t i = t->row_begin; i < t->row_end; i++) {
+        double *c = C + i * t->N;
+        double *s = t->S ? t->S + i * t->N : NULL;
+        for (int64_t j = 0; j < t->N; j++) {
+            c[j] = 0.0;
+            if (s)
+                s[j] = 0.0;
+        }
+        for (int64_t k = 0; k < t->K; k++) {
+            double a = (double)A[i * t->lda + k];
+            const float *b = B + k * t->ldb;
+            for (int64_t j = 0; j < t->N; j++) {
+                double p = a * (double)b[j];
+                c[j] += p;
+                if (s)
+                    s[j] += fabs(p);
+            }
+        }
+    }
+}
+
 static void *band_main(void *arg)
 {
     const band_t *t = (const band_t *)arg;
     if (t->kind == 0)
         band_i8(t);
-    else
+    else if (t->kind == 1)
         band_f16(t);
+    else
+        band_f32(t);
     return NULL;
 }
 
@@ -216,6 +251,16 @@ int oracle_gemm_f16f64(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64
     return run_bands(1, M, N, K, A, lda, B, ldb, C, S, nthreads);
 }
 
+/* C (M x N, dense double) = A (M x K binary32, lda) . B (K x N, ldb);
+ * S (M x N, dense double, may be NULL) = sum_k |A[i][k] * B[k][j]|. */
+int oracle_gemm_f32f64(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                       const float *B, int64_t ldb, double *C, double *S, int nthreads)
+{
+    if (check_args(M, N, K, A, lda, B, ldb, C))
+        return -1;
+    return run_bands(2, M, N, K, A, lda, B, ldb, C, S, nthreads);
+}
+
 /* Single elements of the same product, for matrices too large to multiply
  * whole on the CPU: for each t < count, out[t] = sum_k A[rows[t]][k] *
  * B[k][cols[t]] (increasing k), exactly the value the full routine would put
@@ -252,6 +297,29 @@ int oracle_gemm_f16f64_at(int64_t M, int64_t N, int64_t K, const uint16_t *A, in
         double acc = 0.0, sc = 0.0;
         for (int64_t k = 0; k < K; k++) {
             double p = f16_table[A[i * lda + k]] * f16_table[B[k * ldb + j]];
+            acc += p;
+            sc += fabs(p);
+        }
+        out[t] = acc;
+        if (out_s)
+            out_s[t] = sc;
+    }
+    return 0;
+}
+
+int oracle_gemm_f32f64_at(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, const int64_t *rows, const int64_t *cols,
+                          int64_t count, double *out, double *out_s)
+{
+    if (check_args(M, N, K, A, lda, B, ldb, out))
+        return -1;
+    for (int64_t t = 0; t < count; t++) {
+        int64_t i = rows[t], j = cols[t];
+        if (i < 0 || i >= M || j < 0 || j >= N)
+            return -1;
+        double acc = 0.0, sc = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double p = (double)A[i * lda + k] * (double)B[k * ldb + j];
             acc += p;
             sc += fabs(p);
         }

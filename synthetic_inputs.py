@@ -9,7 +9,8 @@ machine:
 * binary16 operands are a float32 draw rounded to the nearest binary16
   (numpy's ``astype(np.float16)``, round-to-nearest-even), returned as the
   raw uint16 bit patterns the GPU library takes;
-* int8 operands are uniform integers on [-128, 127] inclusive.
+* int8 operands are uniform integers on [-128, 127] inclusive;
+* binary32 operands are the float32 draws themselves.
 
 The pages measure a 4096 x 4096 x 4096 integer GEMM ("Pipeline GPU Kernel",
 Step 2 and Step 6) and name no dataset; the five workloads below are that
@@ -41,6 +42,18 @@ def f16_integers(rows: int, cols: int, seed: int, lo: int = -8, hi: int = 8) -> 
     return rng.integers(lo, hi + 1, size=(rows, cols)).astype(np.float16).view(np.uint16)
 
 
+def f32_normal(rows: int, cols: int, seed: int) -> np.ndarray:
+    """N(0, 1) float32 draws, shape (rows, cols)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((rows, cols), dtype=np.float32)
+
+
+def f32_integers(rows: int, cols: int, seed: int, lo: int = -8, hi: int = 8) -> np.ndarray:
+    """Integers uniform on [lo, hi] inclusive, as float32 (exact)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=(rows, cols)).astype(np.float32)
+
+
 def i8_uniform(rows: int, cols: int, seed: int) -> np.ndarray:
     """int8 uniform on [-128, 127] inclusive."""
     rng = np.random.default_rng(seed)
@@ -50,7 +63,7 @@ def i8_uniform(rows: int, cols: int, seed: int) -> np.ndarray:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str          # "i8" (INT8 in, INT32 out) or "f16" (FP16 in, FP32 out)
+    dtype: str          # "i8" (INT8 in, INT32 out), "f16" (FP16 in, FP32 out), "f32"
     M: int
     N: int
     K: int
@@ -62,6 +75,8 @@ class Workload:
         """(A, B) host arrays: A is M x K, B is K x N, row-major."""
         if self.dist == "uniform_i8":
             return i8_uniform(self.M, self.K, self.seed_a), i8_uniform(self.K, self.N, self.seed_b)
+        if self.dist == "normal" and self.dtype == "f32":
+            return f32_normal(self.M, self.K, self.seed_a), f32_normal(self.K, self.N, self.seed_b)
         if self.dist == "normal":
             return f16_normal(self.M, self.K, self.seed_a), f16_normal(self.K, self.N, self.seed_b)
         if self.dist == "uniform_pm1":
