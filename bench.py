@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 import synthetic_inputs as si  # noqa: E402
 
 METRIC = "GEMM TFLOPS/TOPS at 4096³ (FP16, INT8) + % of MFMA peak; skinny GB/s % HBM"
-PEAK = {"f16": 2500.0, "i8": 5000.0}   # dense MFMA, TFLOP/s and TOP/s
+PEAK = {"f16": 2500.0, "i8": 5000.0, "f32": 157.3}   # dense MFMA, TFLOP/s and TOP/s
 HBM_PEAK_GBS = 8000.0
 
 
@@ -90,7 +90,11 @@ def parse():
 def device_operands(wl):
     import torch
     A, B = wl.operands()
-    if wl.dtype == "f16":
+    if wl.dtype == "f32":
+        dA = torch.from_numpy(A).cuda()
+        dB = torch.from_numpy(B).cuda()
+        C = torch.empty((wl.M, wl.N), dtype=torch.float32, device="cuda")
+    elif wl.dtype == "f16":
         dA = torch.from_numpy(A.view(np.int16)).cuda().view(torch.float16)
         dB = torch.from_numpy(B.view(np.int16)).cuda().view(torch.float16)
         C = torch.empty((wl.M, wl.N), dtype=torch.float32, device="cuda")
@@ -102,17 +106,19 @@ def device_operands(wl):
 
 
 def launcher(tdg, wl, dA, dB, C, variant: str):
-    f16 = wl.dtype == "f16"
+    fns = {"f16": (tdg.gemm_f16f32, tdg.gemm_f16f32_pipelined, tdg.gemm_f16f32_ex),
+           "i8": (tdg.gemm_i8i32, tdg.gemm_i8i32_pipelined, tdg.gemm_i8i32_ex),
+           "f32": (tdg.gemm_f32f32, tdg.gemm_f32f32_pipelined, tdg.gemm_f32f32_ex)}[wl.dtype]
     if variant == "pipelined":
-        fn = tdg.gemm_f16f32_pipelined if f16 else tdg.gemm_i8i32_pipelined
+        fn = fns[1]
         return lambda: fn(dA, dB, C)
     if variant == "single":
-        fn = tdg.gemm_f16f32 if f16 else tdg.gemm_i8i32
+        fn = fns[0]
         return lambda: fn(dA, dB, C)
     cfg = {"reg_s1": dict(variant=tdg.TDG_VARIANT_REG_PREFETCH, lds_stages=1),
            "reg_s2": dict(variant=tdg.TDG_VARIANT_REG_PREFETCH, lds_stages=2),
            "direct": dict(variant=tdg.TDG_VARIANT_DIRECT_LDS, lds_stages=2)}[variant]
-    fn = tdg.gemm_f16f32_ex if f16 else tdg.gemm_i8i32_ex
+    fn = fns[2]
     return lambda: fn(dA, dB, C, cfg=cfg)
 
 
@@ -149,9 +155,14 @@ def individual_launches(run, count: int = 50) -> dict:
             "max_us": round(us[-1], 2)}
 
 
+ELEM_BYTES = {"f16": 2, "i8": 1, "f32": 4}
+UNITS = {"f16": "TFLOP/s", "i8": "TOP/s", "f32": "TFLOP/s"}
+DTYPE_CODE = {"f16": 0, "i8": 1, "f32": 2}
+
+
 def throughput(wl, ms: float):
     ops = 2.0 * wl.M * wl.N * wl.K
-    es = 2 if wl.dtype == "f16" else 1
+    es = ELEM_BYTES[wl.dtype]
     alg_bytes = (wl.M * wl.K + wl.K * wl.N) * es + wl.M * wl.N * 4
     return ops / (ms * 1e-3) / 1e12, alg_bytes / (ms * 1e-3) / 1e9
 
@@ -185,15 +196,16 @@ def transpose_ladder(tdg):
 
 def measured_ceilings(tdg, ladder):
     """Second denominators: the MFMA rate the chip sustains with no memory
-    traffic (tdg_mfma_probe, ~50 ms per launch so the power controller
-    settles) and the bandwidth of the library's copy on a matrix far larger
-    than the last-level cache."""
+    traffic (tdg_mfma_probe, ~20 ms per launch, 5 launches after 2, so the
+    power controller settles) and the bandwidth of the library's copy on a
+    matrix far larger than the last-level cache."""
     import torch
     out = {}
     sink = torch.empty(tdg.tdg_mfma_probe_sink_floats(), dtype=torch.float32, device="cuda")
-    for code, key, iters in ((tdg.TDG_DTYPE_F16F32, "mfma_f16_tflops", 200),
-                             (tdg.TDG_DTYPE_I8I32, "mfma_i8_tops", 100)):
-        ms = time_launches(lambda: tdg.tdg_mfma_probe(code, iters, sink), 4, 1)
+    for code, key, iters in ((tdg.TDG_DTYPE_F16F32, "mfma_f16_tflops", 80000),
+                             (tdg.TDG_DTYPE_I8I32, "mfma_i8_tops", 80000),
+                             (tdg.TDG_DTYPE_F32F32, "mfma_f32_tflops", 40000)):
+        ms = time_launches(lambda: tdg.tdg_mfma_probe(code, iters, sink), 5, 2)
         out[key] = round(tdg.tdg_mfma_probe_ops(code, iters) / (ms * 1e-3) / 1e12, 1)
     if ladder and "16384x16384" in ladder:
         out["copy_gbs"] = ladder["16384x16384"]["copy"]["gbs"]
@@ -206,7 +218,7 @@ def cpu_baseline(wl, A, B, target_s: float):
     R chosen so the run takes about target_s seconds on this host."""
     import oracle
     threads = oracle.host_threads()
-    fn = oracle.gemm_f16 if wl.dtype == "f16" else oracle.gemm_i8
+    fn = {"f16": oracle.gemm_f16, "i8": oracle.gemm_i8, "f32": oracle.gemm_f32}[wl.dtype]
     probe_rows = max(threads, 16)
     t0 = time.perf_counter()
     fn(A[:probe_rows], B, threads=threads)
@@ -217,7 +229,7 @@ def cpu_baseline(wl, A, B, target_s: float):
     fn(A[:rows], B, threads=threads)
     secs = time.perf_counter() - t0
     tops = 2.0 * rows * wl.N * wl.K / secs / 1e12
-    unit = "TFLOP/s" if wl.dtype == "f16" else "TOP/s"
+    unit = UNITS[wl.dtype]
     return {"value": tops, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": "rows 0..%d of C (%d x %d x %d, %.1f s)" % (rows - 1, rows, wl.N, wl.K, secs)}
 
@@ -241,9 +253,8 @@ def main():
     ms = time_launches(run, args.steps, args.warmup)
     tops, gbs = throughput(wl, ms)
     launches = individual_launches(run)
-    dcode = tdg.TDG_DTYPE_F16F32 if wl.dtype == "f16" else tdg.TDG_DTYPE_I8I32
-    cfg, info = tdg.tdg_plan(dcode, wl.M, wl.N, wl.K)
-    unit = "TFLOP/s" if wl.dtype == "f16" else "TOP/s"
+    cfg, info = tdg.tdg_plan(DTYPE_CODE[wl.dtype], wl.M, wl.N, wl.K)
+    unit = UNITS[wl.dtype]
     print("# %s pipelined (%s, %dx%dx%d, %d waves): %.4f ms/launch, %.1f %s"
           % (wl.name, tdg.VARIANT_NAMES[cfg["variant"]], cfg["bm"], cfg["bn"], cfg["bk"],
              cfg["waves"], ms, tops, unit), file=sys.stderr, flush=True)
@@ -285,13 +296,13 @@ def main():
         cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
         tdg.VARIANT_NAMES[cfg["variant"]])
     traffic = profiled_traffic(kernel_desc)
-    es = 2 if wl.dtype == "f16" else 1
-    alg_bytes = (wl.M * wl.K + wl.K * wl.N) * es + wl.M * wl.N * 4
+    alg_bytes = (wl.M * wl.K + wl.K * wl.N) * ELEM_BYTES[wl.dtype] + wl.M * wl.N * 4
     bound = roofline_bound(2.0 * wl.M * wl.N * wl.K, alg_bytes, PEAK[wl.dtype] * 1e3,
                            HBM_PEAK_GBS)
     if bound == "mfma":
         achieved, peak, r_unit = round(tops, 2), PEAK[wl.dtype], unit
-        measured = ceilings.get("mfma_f16_tflops" if wl.dtype == "f16" else "mfma_i8_tops")
+        measured = ceilings.get({"f16": "mfma_f16_tflops", "i8": "mfma_i8_tops",
+                                 "f32": "mfma_f32_tflops"}[wl.dtype])
     else:
         achieved, peak, r_unit = round(gbs, 1), HBM_PEAK_GBS, "GB/s"
         measured = ceilings.get("copy_gbs")
@@ -311,7 +322,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
-                   "accumulate": "f32" if wl.dtype == "f16" else "i32",
+                   "accumulate": "i32" if wl.dtype == "i8" else "f32",
                    "kernel": kernel_desc,
                    "parallelism": "none"},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak,

@@ -10,7 +10,10 @@
  * FP16 entry points take binary16 inputs as raw 16-bit patterns and write
  * FP32 results accumulated in FP32; INT8 entry points take int8 inputs and
  * write INT32 results accumulated in INT32 (exact while |C| < 2^31, which
- * holds for every K <= 131071).
+ * holds for every K <= 131071); FP32 entry points take binary32 inputs and
+ * write FP32 results accumulated in FP32 (the pages' third data type,
+ * "Pipeline GPU Kernel", Step 5: FP32 scalar FFMA; on gfx950 it runs on the
+ * matrix cores' v_mfma_f32_32x32x2_f32).
  *
  * The K loop runs in tiles of BK elements staged through on-chip LDS:
  *   - the unpipelined entry points run the sequential baseline: load tile t,
@@ -66,7 +69,8 @@ typedef enum {
 
 typedef enum {
     TDG_DTYPE_F16F32 = 0, /* binary16 inputs, FP32 accumulate and output */
-    TDG_DTYPE_I8I32 = 1   /* int8 inputs, INT32 accumulate and output */
+    TDG_DTYPE_I8I32 = 1,  /* int8 inputs, INT32 accumulate and output */
+    TDG_DTYPE_F32F32 = 2  /* binary32 inputs, FP32 accumulate and output */
 } tdg_dtype;
 
 typedef enum {
@@ -124,6 +128,11 @@ int gemm_f16f32_pipelined(int64_t M, int64_t N, int64_t K, const uint16_t *A, in
 /* Software-pipelined, double-buffered K loop, INT8 -> INT32. */
 int gemm_i8i32_pipelined(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                          const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
+/* Sequential baseline and pipelined loop, FP32 -> FP32. */
+int gemm_f32f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                int64_t ldb, float *C, int64_t ldc, void *stream);
+int gemm_f32f32_pipelined(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, float *C, int64_t ldc, void *stream);
 /* Explicit configuration (tile, waves, LDS stages, variant), for sweeps and
  * side-by-side comparisons.  cfg == NULL behaves like the _pipelined call.
  * Fields left 0 in cfg are filled by the planner.  A configuration that is
@@ -134,6 +143,9 @@ int gemm_f16f32_ex(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t l
 int gemm_i8i32_ex(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                   const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream,
                   const tdg_config *cfg);
+int gemm_f32f32_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                   const float *B, int64_t ldb, float *C, int64_t ldc, void *stream,
+                   const tdg_config *cfg);
 
 /* Planner.  Chooses the configuration the _pipelined call would run for this
  * dtype and shape (variant = TDG_VARIANT_AUTO), or, when `out` holds a
@@ -200,16 +212,18 @@ int tdg_transpose_f32(int method, int64_t rows, int64_t cols, const float *in, i
 
 /* ---- Measured compute ceiling ("Analyze Kernel Bottleneck", Step 2: set
  * achieved throughput against what the hardware sustains).  Launches a kernel
- * that issues only the GEMM's MFMA instruction (v_mfma_f32_32x32x16_f16 or
- * v_mfma_i32_32x32x32_i8) with changing pseudo-random operands and no memory
+ * that issues only the GEMM's MFMA instruction (v_mfma_f32_32x32x16_f16,
+ * v_mfma_i32_32x32x32_i8 or v_mfma_f32_32x32x2_f32) with changing
+ * pseudo-random operands and no memory
  * traffic: 512 workgroups of 4 waves (two waves per SIMD on 256 CUs), each
- * wave `iters` x 8 MFMAs on eight independent accumulators.  iters must be a
+ * wave `iters` x 8 MFMAs on eight independent accumulators (80000 iters of
+ * the FP16 MFMA is about 20 ms on MI355X).  iters must be a
  * non-negative multiple of 4.  `sink` is a device buffer of
  * tdg_mfma_probe_sink_floats() floats the kernel writes (so the work is not
  * optimised away).  Returns TDG_ERR_INVALID_ARG for a bad dtype, iters or a
  * NULL sink; TDG_ERR_NO_DEVICE off gfx950.  tdg_mfma_probe_ops gives the
- * operations one launch performs (2 * 32 * 32 * k per MFMA), or -1 for bad
- * arguments; time a launch and divide. */
+ * operations one launch performs (2 * 32 * 32 * k per MFMA, k = 16, 32 or 2),
+ * or -1 for bad arguments; time a launch and divide. */
 int tdg_mfma_probe(int dtype, int64_t iters, float *sink, void *stream);
 int64_t tdg_mfma_probe_ops(int dtype, int64_t iters);
 int64_t tdg_mfma_probe_sink_floats(void);

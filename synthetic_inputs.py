@@ -99,4 +99,6 @@ WORKLOADS = {
     # a ragged neighbour of the 4096^3 workload: no dimension a tile multiple,
     # N and K whole 16-byte chunks (the bounds-checked direct-to-LDS loop)
     "fp16_ragged": _wl(6, "fp16_ragged", "f16", 4000, 4000, 4000, "normal"),
+    # the pages' third data type (FP32 in, FP32 accumulate) at the headline shape
+    "fp32_4096": _wl(7, "fp32_4096", "f32", 4096, 4096, 4096, "normal"),
 }

@@ -11,6 +11,7 @@ import oracle
 
 F16 = "f16"
 I8 = "i8"
+F32 = "f32"
 
 
 def to_device(x: np.ndarray):
@@ -26,9 +27,10 @@ def gemm(lib, dtype: str, kind: str, A, B, C=None, cfg=None):
     fn = {
         (F16, "single"): lib.gemm_f16f32, (I8, "single"): lib.gemm_i8i32,
         (F16, "pipelined"): lib.gemm_f16f32_pipelined, (I8, "pipelined"): lib.gemm_i8i32_pipelined,
+        (F32, "single"): lib.gemm_f32f32, (F32, "pipelined"): lib.gemm_f32f32_pipelined,
     }.get((dtype, kind))
     if kind == "ex":
-        ex = lib.gemm_f16f32_ex if dtype == F16 else lib.gemm_i8i32_ex
+        ex = {F16: lib.gemm_f16f32_ex, I8: lib.gemm_i8i32_ex, F32: lib.gemm_f32f32_ex}[dtype]
         return ex(A, B, C, cfg=cfg)
     return fn(A, B, C)
 
@@ -46,6 +48,18 @@ def check_f16(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False):
     """FP16 -> FP32 within |err| <= 1e-4 * sum_k |a_ik b_kj| per element
     (exactly equal when `exact`)."""
     ref, S = oracle.gemm_f16(A, B)
+    got = C_gpu.cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    tol = 0.0 if exact else 1e-4
+    bad = np.argwhere(err > tol * S)
+    assert bad.size == 0, "%d elements out of tolerance, first at %s: got %r want %r (S=%r)" % (
+        len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])], S[tuple(bad[0])])
+
+
+def check_f32(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False):
+    """FP32 -> FP32 within |err| <= 1e-4 * sum_k |a_ik b_kj| per element
+    (exactly equal when `exact`)."""
+    ref, S = oracle.gemm_f32(A, B)
     got = C_gpu.cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
     tol = 0.0 if exact else 1e-4
@@ -79,7 +93,8 @@ def check_sampled(C_gpu, dtype: str, A: np.ndarray, B: np.ndarray, rows, cols):
         assert bad.size == 0, "%d sampled mismatches, first (%d,%d): got %d want %d" % (
             bad.size, rows[bad[0]], cols[bad[0]], got[bad[0]], ref[bad[0]])
     else:
-        ref, S = oracle.gemm_f16_at(A, B, rows, cols)
+        at = oracle.gemm_f32_at if dtype == F32 else oracle.gemm_f16_at
+        ref, S = at(A, B, rows, cols)
         err = np.abs(got.astype(np.float64) - ref)
         bad = np.nonzero(err > 1e-4 * S)[0]
         assert bad.size == 0, "%d sampled out of tolerance, first (%d,%d): got %r want %r" % (

@@ -112,7 +112,8 @@ def test_mfma_probe_arguments():
     assert lib.tdg_mfma_probe(7, 4, 4096, None) == tdg.TDG_ERR_INVALID_ARG
     assert lib.tdg_mfma_probe(0, 3, 4096, None) == tdg.TDG_ERR_INVALID_ARG
     assert lib.tdg_mfma_probe(0, 4, None, None) == tdg.TDG_ERR_INVALID_ARG
-    assert tdg.tdg_mfma_probe_ops(0, 3) == -1 and tdg.tdg_mfma_probe_ops(2, 4) == -1
+    assert tdg.tdg_mfma_probe_ops(0, 3) == -1 and tdg.tdg_mfma_probe_ops(3, 4) == -1
+    assert tdg.tdg_mfma_probe_ops(2, 4) == 2 * 32 * 32 * 2 * 8 * 4 * 2048
     # 512 workgroups x 4 waves x 8 MFMAs per step; 2*32*32*k operations each
     assert tdg.tdg_mfma_probe_ops(0, 4) == 2 * 32 * 32 * 16 * 8 * 4 * 2048
     assert tdg.tdg_mfma_probe_ops(1, 4) == 2 * tdg.tdg_mfma_probe_ops(0, 4)
@@ -208,8 +209,16 @@ def test_planner_choices():
     # the 4000^3 plan keeps the 256x256 tile of the 4096^3 one
     cfg, _ = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4000, 4000, 4000)
     assert (cfg["bm"], cfg["bn"]) == (256, 256)
+    # FP32 inputs: the same 256 x 256 direct-to-LDS plan at 4096^3
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F32F32, 4096, 4096, 4096)
+    assert (cfg["bm"], cfg["bn"], cfg["variant"]) == (256, 256, tdg.TDG_VARIANT_DIRECT_LDS)
+    assert cfg["bk"] == 32 and info["guarded"] == 0 and info["ratio"] == 64.0
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F32F32, 300, 260, 200)
+    assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F32F32, 300, 262, 200)
+    assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH
     # every built configuration can be planned back exactly
-    for code in (0, 1):
+    for code in (0, 1, 2):
         for i in range(tdg.tdg_config_count(code)):
             c = tdg.tdg_config_at(code, i)
             got, _ = tdg.tdg_plan(code, 4 * c["bm"], 4 * c["bn"], 8 * c["bk"], dict(c))

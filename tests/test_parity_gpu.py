@@ -11,9 +11,12 @@ import pytest
 
 import oracle
 import synthetic_inputs as si
-from gpu_util import F16, I8, check_f16, check_i8, check_sampled, gemm, sample_indices, to_device
+from gpu_util import (F16, F32, I8, check_f16, check_f32, check_i8, check_sampled, gemm,
+                      sample_indices, to_device)
 
 pytestmark = pytest.mark.gpu
+
+CODE = {F16: 0, I8: 1, F32: 2}   # tdg_dtype of each test dtype
 
 
 @pytest.fixture(scope="module")
@@ -29,6 +32,10 @@ def lib():
 def _operands(dtype, M, N, K, seed, dist="normal"):
     if dtype == I8:
         return si.i8_uniform(M, K, seed), si.i8_uniform(K, N, seed + 1)
+    if dtype == F32:
+        if dist == "int":
+            return si.f32_integers(M, K, seed), si.f32_integers(K, N, seed + 1)
+        return si.f32_normal(M, K, seed), si.f32_normal(K, N, seed + 1)
     if dist == "int":
         return si.f16_integers(M, K, seed), si.f16_integers(K, N, seed + 1)
     return si.f16_normal(M, K, seed), si.f16_normal(K, N, seed + 1)
@@ -37,6 +44,8 @@ def _operands(dtype, M, N, K, seed, dist="normal"):
 def _check(dtype, C, A, B, exact=False):
     if dtype == I8:
         check_i8(C, A, B)
+    elif dtype == F32:
+        check_f32(C, A, B, exact=exact)
     else:
         check_f16(C, A, B, exact=exact)
 
@@ -45,7 +54,7 @@ def _variants(lib, dtype, tile):
     """Every built loop form (variant x LDS stages) at one tile shape:
     [(name, cfg)], the sequential baseline first."""
     import tiled_dense_gemm_loop_amd as t
-    code = 0 if dtype == F16 else 1
+    code = CODE[dtype]
     out = []
     for i in range(t.tdg_config_count(code)):
         c = t.tdg_config_at(code, i)
@@ -72,7 +81,7 @@ def _tiles(dtype_code):
 
 def _all_tiles():
     try:
-        return [(F16, c) for c in _tiles(0)] + [(I8, c) for c in _tiles(1)]
+        return [(d, c) for d in (F16, I8, F32) for c in _tiles(CODE[d])]
     except ImportError:
         return []
 
@@ -132,7 +141,7 @@ RAGGED = [(1, 1, 1), (5, 7, 3), (64, 64, 1), (33, 65, 17), (300, 290, 333), (257
           (130, 260, 200), (1000, 3, 70), (3, 1000, 129), (64, 64, 63)]
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 @pytest.mark.parametrize("M,N,K", RAGGED)
 def test_ragged_shapes(lib, dtype, M, N, K):
     A, B = _operands(dtype, M, N, K, seed=7 * M + N + K)
@@ -141,12 +150,12 @@ def test_ragged_shapes(lib, dtype, M, N, K):
         _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_ragged_every_tile(lib, dtype):
     M, N, K = 301, 283, 259
     A, B = _operands(dtype, M, N, K, seed=99)
     dA, dB = to_device(A), to_device(B)
-    for tile in (_tiles(0) if dtype == F16 else _tiles(1)):
+    for tile in _tiles(CODE[dtype]):
         for name, cfg in _variants(lib, dtype, tile):
             _check(dtype, gemm(lib, dtype, "ex", dA, dB, cfg=cfg), A, B)
 
@@ -160,13 +169,13 @@ RAGGED_DMA = [(1, 16, 16), (5, 32, 48), (300, 272, 144), (257, 144, 272), (130, 
               (1000, 16, 1040), (64, 64, 16)]
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 @pytest.mark.parametrize("M,N,K", RAGGED_DMA)
 def test_ragged_direct_shapes(lib, dtype, M, N, K):
     import torch
     A, B = _operands(dtype, M, N, K, seed=3 * M + N + K)
     dA, dB = to_device(A), to_device(B)
-    code = 0 if dtype == F16 else 1
+    code = CODE[dtype]
     cfg, info = lib.tdg_plan(code, M, N, K)
     assert info["guarded"] == 1 and cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS
     C = gemm(lib, dtype, "pipelined", dA, dB)
@@ -175,7 +184,7 @@ def test_ragged_direct_shapes(lib, dtype, M, N, K):
     assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_ragged_direct_every_tile(lib, dtype):
     """Every tile and every ring depth asked for on a ragged, chunk-aligned
     shape: all forms agree bit for bit and with the oracle."""
@@ -183,7 +192,7 @@ def test_ragged_direct_every_tile(lib, dtype):
     M, N, K = 301, 288, 272
     A, B = _operands(dtype, M, N, K, seed=98)
     dA, dB = to_device(A), to_device(B)
-    for tile in (_tiles(0) if dtype == F16 else _tiles(1)):
+    for tile in _tiles(CODE[dtype]):
         ref_out = None
         for name, cfg in _variants(lib, dtype, tile):
             C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
@@ -194,7 +203,7 @@ def test_ragged_direct_every_tile(lib, dtype):
                 assert torch.equal(ref_out, C), "%s differs at tile %s" % (name, tile)
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_ragged_direct_padded_rows(lib, dtype):
     """Leading dimensions wider than the matrix (still 16-byte multiples)
     on the ragged direct path: nothing past a row's K or N is used."""
@@ -207,13 +216,13 @@ def test_ragged_direct_padded_rows(lib, dtype):
     _check(dtype, C, A, B)
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_k_zero_writes_zeros(lib, dtype):
     import torch
     M, N = 300, 260
-    A = np.zeros((M, 0), dtype=np.uint16 if dtype == F16 else np.int8)
+    A = np.zeros((M, 0), dtype={F16: np.uint16, I8: np.int8, F32: np.float32}[dtype])
     B = np.zeros((0, N), dtype=A.dtype)
-    out_t = torch.float32 if dtype == F16 else torch.int32
+    out_t = torch.int32 if dtype == I8 else torch.float32
     for kind in ("single", "pipelined"):
         C = torch.full((M, N), 7, dtype=out_t, device="cuda")
         gemm(lib, dtype, kind, to_device(A), to_device(B), C)
@@ -229,7 +238,7 @@ def test_empty_outputs_are_noops(lib):
         assert C.shape == (M, N)
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_strided_and_misaligned_operands(lib, dtype):
     """Leading dimensions wider than the matrix, and base pointers that are
     not 16-byte aligned: the fast path must be skipped, results unchanged."""
@@ -268,6 +277,15 @@ def test_integer_valued_fp16_is_exact(lib):
             check_f16(gemm(lib, F16, kind, dA, dB), A, B, exact=True)
 
 
+def test_integer_valued_fp32_is_exact(lib):
+    """The same pin for FP32 inputs: layout and indexing with no tolerance."""
+    for (M, N, K) in [(1024, 1024, 1024), (512, 768, 640), (300, 288, 336), (300, 290, 333)]:
+        A, B = _operands(F32, M, N, K, seed=M + 3 * N, dist="int")
+        dA, dB = to_device(A), to_device(B)
+        for kind in ("single", "pipelined"):
+            check_f32(gemm(lib, F32, kind, dA, dB), A, B, exact=True)
+
+
 def test_exhaustive_int8_product_table(lib):
     vals = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
     A = vals.reshape(256, 1).copy()
@@ -276,7 +294,7 @@ def test_exhaustive_int8_product_table(lib):
         check_i8(gemm(lib, I8, kind, to_device(A), to_device(B)), A, B)
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_identity(lib, dtype):
     n = 512
     A, _ = _operands(dtype, n, n, n, seed=21)
@@ -284,6 +302,9 @@ def test_identity(lib, dtype):
         one = np.float16(1.0).view(np.uint16)
         I = np.where(np.eye(n, dtype=bool), one, np.uint16(0)).astype(np.uint16)
         expect = A.view(np.float16).astype(np.float32)
+    elif dtype == F32:
+        I = np.eye(n, dtype=np.float32)
+        expect = A
     else:
         I = np.eye(n, dtype=np.int8)
         expect = A.astype(np.int32)
@@ -311,10 +332,13 @@ def test_all_ones_detects_a_dropped_tile(lib):
     """All-ones operands give C = K everywhere; a lost K tile would give K - BK."""
     import torch
     M, N, K = 512, 512, 1024
-    for dtype in (F16, I8):
+    for dtype in (F16, I8, F32):
         if dtype == F16:
             A = np.full((M, K), np.float16(1.0).view(np.uint16), dtype=np.uint16)
             B = np.full((K, N), np.float16(1.0).view(np.uint16), dtype=np.uint16)
+        elif dtype == F32:
+            A = np.ones((M, K), dtype=np.float32)
+            B = np.ones((K, N), dtype=np.float32)
         else:
             A = np.ones((M, K), dtype=np.int8)
             B = np.ones((K, N), dtype=np.int8)
@@ -367,20 +391,20 @@ def test_invalid_arguments_are_rejected(lib):
 
 # --- the full-size workloads, in the configuration the benchmark times ---------------------
 
-@pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny"])
+@pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny", "fp32_4096"])
 def test_full_size_sampled(lib, name):
     import torch
     wl = si.WORKLOADS[name]
     A, B = wl.operands()
     dA, dB = to_device(A), to_device(B)
-    dtype = I8 if wl.dtype == "i8" else F16
+    dtype = {"i8": I8, "f16": F16, "f32": F32}[wl.dtype]
     rows, cols = sample_indices(wl.M, wl.N, 3000, seed=wl.seed_a, tile_n=min(256, wl.N))
     C_pipe = gemm(lib, dtype, "pipelined", dA, dB)
     check_sampled(C_pipe, dtype, A, B, rows, cols)
     C_single = gemm(lib, dtype, "single", dA, dB)
     check_sampled(C_single, dtype, A, B, rows, cols)
     assert torch.equal(C_pipe, C_single)
-    tile, _ = lib.tdg_plan(0 if dtype == F16 else 1, wl.M, wl.N, wl.K)
+    tile, _ = lib.tdg_plan(CODE[dtype], wl.M, wl.N, wl.K)
     for vname, cfg in _variants(lib, dtype, tile):
         assert torch.equal(C_pipe, gemm(lib, dtype, "ex", dA, dB, cfg=cfg)), vname
     del C_pipe, C_single, dA, dB
@@ -388,7 +412,7 @@ def test_full_size_sampled(lib, name):
 
 
 @pytest.mark.parametrize("dtype,M,N,K", [(F16, 4000, 4000, 4000), (I8, 4000, 4000, 4000),
-                                         (F16, 16383, 64, 8184)])
+                                         (F16, 16383, 64, 8184), (F32, 4000, 4000, 4000)])
 def test_large_ragged_sampled(lib, dtype, M, N, K):
     """Ragged shapes near the benchmark sizes run the bounds-checked
     direct-to-LDS loop; sampled elements (tile edges included) against the
@@ -396,7 +420,7 @@ def test_large_ragged_sampled(lib, dtype, M, N, K):
     import torch
     A, B = _operands(dtype, M, N, K, seed=M + K)
     dA, dB = to_device(A), to_device(B)
-    code = 0 if dtype == F16 else 1
+    code = CODE[dtype]
     cfg, info = lib.tdg_plan(code, M, N, K)
     assert info["guarded"] == 1 and cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS
     rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=min(cfg["bn"], N))

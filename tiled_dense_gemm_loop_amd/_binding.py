@@ -21,6 +21,7 @@ TDG_ERR_NO_DEVICE = -4
 
 TDG_DTYPE_F16F32 = 0
 TDG_DTYPE_I8I32 = 1
+TDG_DTYPE_F32F32 = 2
 
 TDG_VARIANT_AUTO = 0
 TDG_VARIANT_SINGLE = 1
@@ -41,7 +42,8 @@ TRANSPOSE_NAMES = {1: "naive", 2: "lds", 3: "lds_padded", 4: "lds_swizzled", 5: 
 # Every symbol include/tdgemm.h declares.
 EXPORTED = (
     "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
-    "gemm_f16f32_ex", "gemm_i8i32_ex", "tdg_plan", "tdg_tile_figures", "tdg_config_count",
+    "gemm_f16f32_ex", "gemm_i8i32_ex", "gemm_f32f32", "gemm_f32f32_pipelined", "gemm_f32f32_ex",
+    "tdg_plan", "tdg_tile_figures", "tdg_config_count",
     "tdg_config_at", "tdg_status_string", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
 )
@@ -93,11 +95,12 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
-    for name in ("gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined"):
+    for name in ("gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
+                 "gemm_f32f32", "gemm_f32f32_pipelined"):
         fn = getattr(lib, name)
         fn.argtypes = gemm_args
         fn.restype = c_int
-    for name in ("gemm_f16f32_ex", "gemm_i8i32_ex"):
+    for name in ("gemm_f16f32_ex", "gemm_i8i32_ex", "gemm_f32f32_ex"):
         fn = getattr(lib, name)
         fn.argtypes = gemm_args + [ctypes.POINTER(TdgConfig)]
         fn.restype = c_int
@@ -166,15 +169,19 @@ def _matrix(t, dtypes, what):
 
 
 def _gemm(name, A, B, C, cfg, f16):
+    """f16: True (binary16 in), False (int8 in) or "f32" (binary32 in)."""
     torch = _torch()
-    in_types = (torch.float16, torch.int16) if f16 else (torch.int8,)
+    if f16 == "f32":
+        in_types = (torch.float32,)
+    else:
+        in_types = (torch.float16, torch.int16) if f16 else (torch.int8,)
     M, K, pa, lda = _matrix(A, in_types, "A")
     K2, N, pb, ldb = _matrix(B, in_types, "B")
     if K != K2:
         raise ValueError("inner dimensions differ: A is %dx%d, B is %dx%d" % (M, K, K2, N))
     if A.device != B.device:
         raise ValueError("A and B are on different devices")
-    out_type = torch.float32 if f16 else torch.int32
+    out_type = torch.float32 if f16 else torch.int32  # "f32" is truthy
     if C is None:
         C = torch.empty((M, N), dtype=out_type, device=A.device)
     Mc, Nc, pc, ldc = _matrix(C, (out_type,), "C")
@@ -224,6 +231,20 @@ def gemm_f16f32_ex(A, B, C=None, cfg=None):
 
 def gemm_i8i32_ex(A, B, C=None, cfg=None):
     return _gemm("gemm_i8i32_ex", A, B, C, _cfg(cfg), False)
+
+
+def gemm_f32f32(A, B, C=None):
+    """Sequential single-buffer baseline: C (float32) = A . B (float32)."""
+    return _gemm("gemm_f32f32", A, B, C, None, "f32")
+
+
+def gemm_f32f32_pipelined(A, B, C=None):
+    """Software-pipelined double-buffered K loop, FP32 -> FP32."""
+    return _gemm("gemm_f32f32_pipelined", A, B, C, None, "f32")
+
+
+def gemm_f32f32_ex(A, B, C=None, cfg=None):
+    return _gemm("gemm_f32f32_ex", A, B, C, _cfg(cfg), "f32")
 
 
 def tdg_plan(dtype: int, M: int, N: int, K: int, cfg=None):

@@ -1,6 +1,6 @@
 """Build libtdgemm.so, the gfx950 GEMM library, in-tree with hipcc.
 
-The kernel tables for the two dtypes are separate translation units and are
+The kernel tables for the three dtypes are separate translation units and are
 compiled in parallel with the host API and the copy/transpose ladder.  All
 HIP code is compiled for gfx950 only, with packed-FP32 instruction selection
 turned off.
@@ -28,6 +28,7 @@ COMMON = [
 UNITS = [
     ("tdg_kernels.hip", ["-DTDG_BUILD_DT=0"], "tdg_kernels_f16.o"),
     ("tdg_kernels.hip", ["-DTDG_BUILD_DT=1"], "tdg_kernels_i8.o"),
+    ("tdg_kernels.hip", ["-DTDG_BUILD_DT=2"], "tdg_kernels_f32.o"),
     ("tdg_api.hip", [], "tdg_api.o"),
     ("tdg_move.hip", [], "tdg_move.o"),
     ("tdg_probe.hip", [], "tdg_probe.o"),

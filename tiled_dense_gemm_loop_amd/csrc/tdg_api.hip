@@ -22,11 +22,13 @@ const KernelEntry *kernel_table(int *count) {
     static int n = 0;
     static std::once_flag once;
     std::call_once(once, [] {
-        int nf = 0, ni = 0;
+        int nf = 0, ni = 0, n32 = 0;
         const KernelEntry *f = kernel_table_f16(&nf);
         const KernelEntry *i = kernel_table_i8(&ni);
+        const KernelEntry *w = kernel_table_f32(&n32);
         for (int k = 0; k < nf && n < 256; k++) all[n++] = f[k];
         for (int k = 0; k < ni && n < 256; k++) all[n++] = i[k];
+        for (int k = 0; k < n32 && n < 256; k++) all[n++] = w[k];
     });
     *count = n;
     return all;
@@ -61,7 +63,13 @@ constexpr int kLdsPerCU = 160 * 1024;     // gfx950 LDS per CU
 constexpr int kWaveSlotsPerCU = 4 * 8;    // 4 SIMDs x 8 wave slots
 constexpr int kRegsPerLanePerSIMD = 512;  // unified VGPR + AGPR file
 
-int elem_size(int dtype) { return dtype == TDG_DTYPE_F16F32 ? 2 : 1; }
+int elem_size(int dtype) {
+    return dtype == TDG_DTYPE_F16F32 ? 2 : (dtype == TDG_DTYPE_I8I32 ? 1 : 4);
+}
+
+bool dtype_ok(int dtype) {
+    return dtype == TDG_DTYPE_F16F32 || dtype == TDG_DTYPE_I8I32 || dtype == TDG_DTYPE_F32F32;
+}
 
 // ---------------------------------------------------------------- validation
 
@@ -78,7 +86,7 @@ uint64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
 
 int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
              int64_t ldb, const void *C, int64_t ldc) {
-    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return TDG_ERR_INVALID_ARG;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return TDG_ERR_INVALID_ARG;
     if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
@@ -435,8 +443,26 @@ int gemm_i8i32_ex(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
     return run(TDG_DTYPE_I8I32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, true);
 }
 
+int gemm_f32f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                int64_t ldb, float *C, int64_t ldc, void *stream) {
+    tdg_config cfg;
+    memset(&cfg, 0, sizeof(cfg));
+    cfg.variant = TDG_VARIANT_SINGLE;
+    return run(TDG_DTYPE_F32F32, M, N, K, A, lda, B, ldb, C, ldc, stream, &cfg, false);
+}
+
+int gemm_f32f32_pipelined(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+    return run(TDG_DTYPE_F32F32, M, N, K, A, lda, B, ldb, C, ldc, stream, nullptr, true);
+}
+
+int gemm_f32f32_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                   int64_t ldb, float *C, int64_t ldc, void *stream, const tdg_config *cfg) {
+    return run(TDG_DTYPE_F32F32, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg, true);
+}
+
 int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info) {
-    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
         return TDG_ERR_INVALID_ARG;
     tdg_config req;
@@ -452,7 +478,7 @@ int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_pl
 
 int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant,
                      int64_t M, int64_t N, int64_t K, tdg_plan_info *info) {
-    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
     if (bm <= 0 || bn <= 0 || bk <= 0 || waves <= 0 || waves > 16) return TDG_ERR_INVALID_ARG;
     if (stages < 1 || stages > 8 || M < 0 || N < 0 || K < 0 || !info) return TDG_ERR_INVALID_ARG;
     tile_figures(dtype, bm, bn, bk, waves, stages, variant, M, N, K, info);

@@ -5,7 +5,7 @@ namespace tdg {
 
 // One built kernel: its tile shape, loop form and launch needs.
 struct KernelEntry {
-    int dtype;      // 0 = FP16 -> FP32, 1 = INT8 -> INT32
+    int dtype;      // 0 = FP16 -> FP32, 1 = INT8 -> INT32, 2 = FP32 -> FP32
     int bm, bn;     // C tile
     int bkb;        // K tile in bytes per row (BK = bkb / sizeof(T))
     int wm, wn;     // wave grid; waves = wm * wn
@@ -20,6 +20,7 @@ struct KernelEntry {
 // Per-dtype tables (one translation unit each) and their concatenation.
 const KernelEntry *kernel_table_f16(int *count);
 const KernelEntry *kernel_table_i8(int *count);
+const KernelEntry *kernel_table_f32(int *count);
 const KernelEntry *kernel_table(int *count);
 
 // TDG_OK when the current device is gfx950, else TDG_ERR_NO_DEVICE.

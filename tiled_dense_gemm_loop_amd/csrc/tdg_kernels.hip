@@ -43,14 +43,28 @@ namespace tdg {
         TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4), TDG_DIRECT(DT, 64, 64, 128, 2, 2, 8),      \
         TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 4)
 
-// Each dtype's table is its own translation unit (TDG_BUILD_DT = 0 or 1), so
-// the two halves compile in parallel.
+// FP32 inputs: v_mfma_f32_32x32x2_f32 does 8x fewer operations per byte of
+// LDS traffic than the FP16 MFMA, so the shapes are the same tiles with fewer
+// rings.  The 4-wave 256 x 256 tile is left out: its 256 accumulator
+// registers plus four MFMAs per K step per block spill.
+#define TDG_SHAPES_F32(DT)                                                                \
+    TDG_SHAPE(DT, 256, 256, 128, 2, 4), TDG_SHAPE(DT, 128, 128, 128, 2, 2),              \
+        TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3),                                          \
+        TDG_SHAPE(DT, 128, 64, 128, 4, 1), TDG_DIRECT(DT, 128, 64, 128, 4, 1, 4),        \
+        TDG_DIRECT_G(DT, 128, 64, 128, 4, 1, 4), TDG_SHAPE(DT, 64, 64, 128, 2, 2),       \
+        TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4), TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 4)
+
+// Each dtype's table is its own translation unit (TDG_BUILD_DT = 0, 1 or 2),
+// so the three compile in parallel.
 #if TDG_BUILD_DT == 0
 static const KernelEntry kTable[] = {TDG_SHAPES(DT_F16)};
 const KernelEntry *kernel_table_f16(int *count) {
-#else
+#elif TDG_BUILD_DT == 1
 static const KernelEntry kTable[] = {TDG_SHAPES(DT_I8)};
 const KernelEntry *kernel_table_i8(int *count) {
+#else
+static const KernelEntry kTable[] = {TDG_SHAPES_F32(DT_F32)};
+const KernelEntry *kernel_table_f32(int *count) {
 #endif
     *count = (int)(sizeof(kTable) / sizeof(kTable[0]));
     return kTable;

@@ -50,7 +50,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define TDG_LDS __attribute__((address_space(3)))
 #define TDG_GLOBAL __attribute__((address_space(1)))
 
-enum { DT_F16 = 0, DT_I8 = 1 };
+enum { DT_F16 = 0, DT_I8 = 1, DT_F32 = 2 };
 enum { VAR_SINGLE = 1, VAR_REG = 2, VAR_DIRECT = 3 };
 
 // Kernel arguments (passed by value).  Leading dimensions are in elements.
@@ -68,7 +68,7 @@ struct GemmArgs {
 // Compile-time geometry of one configuration.
 template <int DT, int BM_, int BN_, int BKB_, int WM_, int WN_>
 struct Geo {
-    static constexpr int ES = DT == DT_F16 ? 2 : 1;  // input element bytes
+    static constexpr int ES = DT == DT_F16 ? 2 : (DT == DT_I8 ? 1 : 4);  // input element bytes
     static constexpr int BM = BM_, BN = BN_, BKB = BKB_;
     static constexpr int BK = BKB / ES;  // K elements per tile
     static constexpr int WM = WM_, WN = WN_;
@@ -87,6 +87,10 @@ struct Geo {
     static constexpr int B_CHUNKS = BK * B_CPR;
     static constexpr int B_BYTES = BK * B_ROWB;
     static constexpr int B_RP = B_ROWB >= 256 ? 1 : 256 / B_ROWB;
+    // B fragments: FP16 / INT8 use gfx950's transposing 8-byte reads (two per
+    // fragment); FP32 has no transposing read and takes four 4-byte reads.
+    static constexpr bool TRB = DT != DT_F32;
+    static constexpr int B_RD = TRB ? 2 : 4;  // LDS reads per B fragment
     // Transposed-read geometry: a 16-lane group reads TR_ROWS k-rows, LPR lanes
     // per row, EPL elements per lane; two adjacent groups read SEG_CH chunks.
     static constexpr int TR_ROWS = DT == DT_F16 ? 4 : 8;
@@ -101,8 +105,8 @@ struct Geo {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0, "tile must split evenly over threads");
     static_assert((B_CPR & (B_CPR - 1)) == 0, "B row must be a power-of-two number of chunks");
-    static_assert(TR_ROWS >= B_RP, "B rows per bank line exceed the transposed-read group");
-    static_assert(SEG_CH * (TR_ROWS / B_RP) <= B_CPR, "B swizzle must stay inside a row");
+    static_assert(!TRB || TR_ROWS >= B_RP, "B rows per bank line exceed the transposed-read group");
+    static_assert(!TRB || SEG_CH * (TR_ROWS / B_RP) <= B_CPR, "B swizzle must stay inside a row");
 
     // Physical 16-byte chunk of logical chunk c in A row r.  Sixteen
     // consecutive rows read at one logical chunk land on 16 distinct
@@ -110,7 +114,9 @@ struct Geo {
     __device__ static __forceinline__ int swz_a(int r) { return (r / A_RP) % A_CPR; }
     // XOR applied to the chunk index of B row k: the TR_ROWS rows that one
     // transposed read touches, SEG_CH chunks each, land on distinct slots.
+    // FP32 reads 4-byte words, half a wave per row: no swizzle needed.
     __device__ static __forceinline__ int swz_b(int k) {
+        if constexpr (!TRB) return 0;
         return ((k / B_RP) % (TR_ROWS / B_RP)) * SEG_CH;
     }
 };
@@ -118,11 +124,14 @@ struct Geo {
 // MFMA operand/accumulator types per dtype.
 template <int DT>
 struct Mfma;
+// One K step (32 bytes of K per lane pair) is SUB MFMAs; mac_sub issues the
+// e-th of them.
 template <>
 struct Mfma<DT_F16> {
     typedef f32x16 acc_t;
     typedef float out_t;
-    __device__ static __forceinline__ acc_t mac(u32x4 a, u32x4 b, acc_t c) {
+    static constexpr int SUB = 1;
+    __device__ static __forceinline__ acc_t mac_sub(u32x4 a, u32x4 b, acc_t c, int) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
@@ -138,7 +147,8 @@ template <>
 struct Mfma<DT_I8> {
     typedef i32x16 acc_t;
     typedef int32_t out_t;
-    __device__ static __forceinline__ acc_t mac(u32x4 a, u32x4 b, acc_t c) {
+    static constexpr int SUB = 1;
+    __device__ static __forceinline__ acc_t mac_sub(u32x4 a, u32x4 b, acc_t c, int) {
         return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
                                                      __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
     }
@@ -147,6 +157,31 @@ struct Mfma<DT_I8> {
         i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TDG_LDS i32x2 *)(p0));
         i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TDG_LDS i32x2 *)(p1));
         return u32x4{(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]};
+    }
+};
+
+// FP32: v_mfma_f32_32x32x2_f32 multiplies one binary32 of A (row l % 32) by
+// one of B (column l % 32) per lane, at k = l / 32 of the instruction's two.
+// A 16-byte A fragment holds a lane's four consecutive k (4h .. 4h+3 of the
+// step's eight, h = l / 32), so the step is four MFMAs, the e-th taking
+// element e of both fragments: it covers k = e and k = 4 + e.
+template <>
+struct Mfma<DT_F32> {
+    typedef f32x16 acc_t;
+    typedef float out_t;
+    static constexpr int SUB = 4;
+    // (The elements go through scalars: a bit cast applied directly to a
+    // vector subscript reads element 0 whatever the index.)
+    __device__ static __forceinline__ acc_t mac_sub(u32x4 a, u32x4 b, acc_t c, int e) {
+        const uint32_t x = a[e], y = b[e];
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, x),
+                                                    __builtin_bit_cast(float, y), c, 0, 0, 0);
+    }
+    // Four 4-byte reads: rows k = 4h + e of the N-contiguous B image.
+    __device__ static __forceinline__ u32x4 read_b4(const unsigned char *p0, const unsigned char *p1,
+                                                    const unsigned char *p2, const unsigned char *p3) {
+        return u32x4{*(const TDG_LDS uint32_t *)p0, *(const TDG_LDS uint32_t *)p1,
+                     *(const TDG_LDS uint32_t *)p2, *(const TDG_LDS uint32_t *)p3};
     }
 };
 
@@ -213,7 +248,9 @@ __device__ static __forceinline__ u32x4 load_chunk_guarded(const unsigned char *
 #pragma unroll
         for (int e = 0; e < EPC; e++) {
             if (e < valid) {
-                uint32_t v = ES == 2 ? (uint32_t)((const uint16_t *)p)[e] : (uint32_t)p[e];
+                uint32_t v = ES == 4   ? ((const uint32_t *)p)[e]
+                             : ES == 2 ? (uint32_t)((const uint16_t *)p)[e]
+                                       : (uint32_t)p[e];
                 w[(e * ES) >> 2] |= v << (((e * ES) & 3) * 8);
             }
         }
@@ -255,7 +292,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     constexpr int A_RSTEP = G::NT / G::A_CPR;
     constexpr int B_RSTEP = G::NT / G::B_CPR;
     static_assert(A_RSTEP % (G::A_RP * G::A_CPR) == 0, "A swizzle must repeat every RSTEP rows");
-    static_assert(B_RSTEP % G::TR_ROWS == 0, "B swizzle must repeat every RSTEP rows");
+    static_assert(!G::TRB || B_RSTEP % G::TR_ROWS == 0, "B swizzle must repeat every RSTEP rows");
     const int64_t lda_b = args.lda * G::ES, ldb_b = args.ldb * G::ES;
     const unsigned char *a_base = args.A + (int64_t)m0 * lda_b;
     const unsigned char *b_base = args.B + (int64_t)n0 * G::ES;
@@ -275,15 +312,20 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
         for (int s = 0; s < G::KSTEPS; s++)
             a_roff[s] = (uint32_t)(r * G::BKB + (((2 * s + (lane >> 5)) ^ G::swz_a(r)) * 16));
     }
-    uint32_t b_roff[G::KSTEPS][2][G::NI];
-    {
+    // FP32 B reads need no swizzle, so every read address is one per-lane
+    // base plus a constant (folded into the instruction's offset field).
+    const uint32_t b_roff32 = (uint32_t)(G::A_BYTES + ((lane >> 5) * 4) * G::B_ROWB +
+                                         (wn * G::WTN + (lane & 31)) * G::ES);
+    uint32_t b_roff[G::TRB ? G::KSTEPS : 1][G::TRB ? G::B_RD : 1][G::NI];
+    if constexpr (G::TRB) {
         constexpr int KS = 32 / G::ES;       // k per MFMA step
         constexpr int KH = KS / 2;           // k per lane half (lane / 32)
         constexpr int KR = G::TR_ROWS;       // k per transposed read
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; s++)
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
+            for (int h = 0; h < G::B_RD; h++) {
+                // k-row group h of the lane's half
                 const int k = s * KS + (lane >> 5) * KH + h * KR + (lane & 15) / G::LPR;
 #pragma unroll
                 for (int ni = 0; ni < G::NI; ni++) {
@@ -415,12 +457,20 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     constexpr int NSETS = FD == 1 ? 2 : G::KSTEPS;
     static_assert(FD == 1 || NSETS == G::KSTEPS, "set index must equal the step index");
     u32x4 fa[NSETS][G::MI], fb[NSETS][G::NI];
+    auto read_bfrag = [&](const unsigned char *st, int s, int ni) -> u32x4 {
+        if constexpr (G::TRB) {
+            return MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
+        } else {
+            // rows k = 8 s + 4 (l / 32) + h, h = 0..3; column block ni
+            const unsigned char *p = st + b_roff32 + (s * 8) * G::B_ROWB + ni * 32 * G::ES;
+            return MM::read_b4(p, p + G::B_ROWB, p + 2 * G::B_ROWB, p + 3 * G::B_ROWB);
+        }
+    };
     auto read_frags = [&](const unsigned char *st, int s, int set) {
 #pragma unroll
         for (int mi = 0; mi < G::MI; mi++) fa[set][mi] = lds_read16(st + a_roff[s] + mi * 32 * G::BKB);
 #pragma unroll
-        for (int ni = 0; ni < G::NI; ni++)
-            fb[set][ni] = MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
+        for (int ni = 0; ni < G::NI; ni++) fb[set][ni] = read_bfrag(st, s, ni);
     };
     // One K step's MFMAs with the fragment reads of a later step (read
     // units: MI A reads, then NI pairs of transposed B reads) and, at a tile
@@ -430,28 +480,31 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // of them from every wave at once queues and holds back each wave's next
     // MFMAs; spread out, each one issues into an idle queue while the MFMA
     // pipe stays busy.
+    // With SUB > 1 (FP32) the step's MFMAs go round-robin over the
+    // accumulators, so dependent MFMAs are NM instructions apart.
     auto step = [&](int cset, const unsigned char *rst, int rstep, int rset, bool reads,
                     uint32_t dma_st, int dma_kt, bool dma) {
         constexpr int NM = G::MI * G::NI, NR = G::MI + G::NI, ND = G::CA + G::CB;
+        constexpr int NMF = NM * MM::SUB;  // MFMA issue slots in the step
 #pragma unroll
-        for (int m = 0; m < NM; m++) {
+        for (int t = 0; t < NMF; t++) {
+            const int m = t % NM, e = t / NM;
             acc[m / G::NI][m % G::NI] =
-                MM::mac(fa[cset][m / G::NI], fb[cset][m % G::NI], acc[m / G::NI][m % G::NI]);
+                MM::mac_sub(fa[cset][m / G::NI], fb[cset][m % G::NI], acc[m / G::NI][m % G::NI], e);
             __builtin_amdgcn_sched_barrier(0);
             if (reads) {
 #pragma unroll
-                for (int u = (m * NR + NM - 1) / NM; u < ((m + 1) * NR + NM - 1) / NM; u++) {
+                for (int u = (t * NR + NMF - 1) / NMF; u < ((t + 1) * NR + NMF - 1) / NMF; u++) {
                     if (u < G::MI) {
                         fa[rset][u] = lds_read16(rst + a_roff[rstep] + u * 32 * G::BKB);
                     } else {
-                        const int ni = u - G::MI;
-                        fb[rset][ni] = MM::read_b(rst + b_roff[rstep][0][ni], rst + b_roff[rstep][1][ni]);
+                        fb[rset][u - G::MI] = read_bfrag(rst, rstep, u - G::MI);
                     }
                 }
             }
             if (dma) {
 #pragma unroll
-                for (int d = (m * ND + NM - 1) / NM; d < ((m + 1) * ND + NM - 1) / NM; d++)
+                for (int d = (t * ND + NMF - 1) / NMF; d < ((t + 1) * ND + NMF - 1) / NMF; d++)
                     issue_direct_one(dma_st, dma_kt, d);
             }
             __builtin_amdgcn_sched_barrier(0);

@@ -34,11 +34,12 @@ __device__ __forceinline__ uint32_t mix(uint32_t x) {
     return x;
 }
 
-// Operand words: random binary16 pairs with exponents near 1.0 (no
-// infinities or NaNs), or random bytes for INT8.
+// Operand words: random binary16 pairs or binary32 values with exponents
+// near 1.0 (no infinities or NaNs), or random bytes for INT8.
 __device__ __forceinline__ uint32_t operand_word(int dtype, uint32_t seed) {
     const uint32_t r = mix(seed);
     if (dtype == TDG_DTYPE_I8I32) return r;
+    if (dtype == TDG_DTYPE_F32F32) return (r & 0x807FFFFFu) | 0x3F000000u;  // 0.5 .. 1
     return (r & 0x83FF83FFu) | 0x38003800u;  // sign, mantissa random; exponent 14 (0.5 .. 1)
 }
 
@@ -71,6 +72,25 @@ __global__ void __launch_bounds__(PROBE_THREADS) k_mfma_probe(int64_t iters, flo
         for (int k = 0; k < 8; k++)
 #pragma unroll
             for (int v = 0; v < 16; v++) total += c[k][v];
+    } else if constexpr (DT == TDG_DTYPE_F32F32) {
+        f32x16 c[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) c[k] = f32x16{};
+        for (int64_t it = 0; it < iters; it += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    // through scalars: a bit cast of a vector subscript reads element 0
+                    const uint32_t x = (uint32_t)a[(k + u) & 3][u], y = (uint32_t)b[(k + 1) & 3][k & 3];
+                    c[k] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, x),
+                                                                __builtin_bit_cast(float, y), c[k], 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) total += c[k][v];
     } else {
         i32x16 c[8];
 #pragma unroll
@@ -96,9 +116,13 @@ __global__ void __launch_bounds__(PROBE_THREADS) k_mfma_probe(int64_t iters, flo
 
 extern "C" {
 
+static bool probe_dtype(int dtype) {
+    return dtype == TDG_DTYPE_F16F32 || dtype == TDG_DTYPE_I8I32 || dtype == TDG_DTYPE_F32F32;
+}
+
 int64_t tdg_mfma_probe_ops(int dtype, int64_t iters) {
-    if ((dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) || iters < 0 || iters % 4) return -1;
-    const int64_t k = dtype == TDG_DTYPE_F16F32 ? 16 : 32;
+    if (!probe_dtype(dtype) || iters < 0 || iters % 4) return -1;
+    const int64_t k = dtype == TDG_DTYPE_F16F32 ? 16 : (dtype == TDG_DTYPE_I8I32 ? 32 : 2);
     const int64_t waves = (int64_t)PROBE_CUS * PROBE_WG_PER_CU * (PROBE_THREADS / 64);
     return 2 * 32 * 32 * k * 8 * iters * waves;
 }
@@ -108,13 +132,14 @@ int64_t tdg_mfma_probe_sink_floats(void) {
 }
 
 int tdg_mfma_probe(int dtype, int64_t iters, float *sink, void *stream) {
-    if (dtype != TDG_DTYPE_F16F32 && dtype != TDG_DTYPE_I8I32) return TDG_ERR_INVALID_ARG;
+    if (!probe_dtype(dtype)) return TDG_ERR_INVALID_ARG;
     if (iters < 0 || iters % 4 || !sink) return TDG_ERR_INVALID_ARG;
     const int dev = tdg::device_check();
     if (dev != TDG_OK) return dev;
     void *kargs[] = {&iters, &sink};
     const void *fn = dtype == TDG_DTYPE_F16F32 ? (const void *)&k_mfma_probe<TDG_DTYPE_F16F32>
-                                               : (const void *)&k_mfma_probe<TDG_DTYPE_I8I32>;
+                     : dtype == TDG_DTYPE_I8I32 ? (const void *)&k_mfma_probe<TDG_DTYPE_I8I32>
+                                                : (const void *)&k_mfma_probe<TDG_DTYPE_F32F32>;
     if (hipLaunchKernel(fn, dim3(PROBE_CUS * PROBE_WG_PER_CU), dim3(PROBE_THREADS), kargs, 0,
                         (hipStream_t)stream) != hipSuccess)
         return TDG_ERR_LAUNCH;
