@@ -160,6 +160,42 @@ UNITS = {"f16": "TFLOP/s", "i8": "TOP/s", "f32": "TFLOP/s"}
 DTYPE_CODE = {"f16": 0, "i8": 1, "f32": 2}
 
 
+def cold_launches(tdg, wl, count: int = 20, scrub_mib: int = 512) -> dict:
+    """Launches that start with cold caches.  Before each one a 512 MiB
+    buffer (more than the 256 MB last-level cache holds) is either read
+    (the caches then hold clean scrub data) or written (they then hold dirty
+    lines, whose write-back the launch also pays for).  Only the launch
+    itself is bracketed by events."""
+    import torch
+    A, B, dA, dB, C = device_operands(wl)
+    run = launcher(tdg, wl, dA, dB, C, "pipelined")
+    scrub = torch.ones(scrub_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    run()
+    out = {"workload": wl.name, "scrub_mib": scrub_mib, "count": count}
+    for mode in ("read", "write"):
+        evs = []
+        for i in range(count):
+            if mode == "read":
+                torch.sum(scrub, dim=0, out=sink)
+            else:
+                scrub.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[count // 2]
+        tops, gbs = throughput(wl, med * 1e-3)
+        out["after_%s_scrub" % mode] = {"median_us": round(med, 2), "min_us": round(us[0], 2),
+                                        "gbs": round(gbs, 1), "tops": round(tops, 1)}
+    del A, B, dA, dB, C, scrub
+    torch.cuda.empty_cache()
+    return out
+
+
 def throughput(wl, ms: float):
     ops = 2.0 * wl.M * wl.N * wl.K
     es = ELEM_BYTES[wl.dtype]
@@ -213,9 +249,21 @@ def measured_ceilings(tdg, ladder):
     return out
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, A, B, target_s: float):
     """The oracle as it stands, on a bounded sample: the first R rows of C,
-    R chosen so the run takes about target_s seconds on this host."""
+    R chosen so the run takes about target_s seconds on this host; plus the
+    same oracle on one thread for the FP16 1024^3 workload (a per-core
+    figure)."""
     import oracle
     threads = oracle.host_threads()
     fn = {"f16": oracle.gemm_f16, "i8": oracle.gemm_i8, "f32": oracle.gemm_f32}[wl.dtype]
@@ -230,8 +278,16 @@ def cpu_baseline(wl, A, B, target_s: float):
     secs = time.perf_counter() - t0
     tops = 2.0 * rows * wl.N * wl.K / secs / 1e12
     unit = UNITS[wl.dtype]
+    small = si.WORKLOADS["fp16_1024"]
+    sa, sb = small.operands()
+    t0 = time.perf_counter()
+    oracle.gemm_f16(sa, sb, threads=1)
+    one = time.perf_counter() - t0
     return {"value": tops, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": "rows 0..%d of C (%d x %d x %d, %.1f s)" % (rows - 1, rows, wl.N, wl.K, secs)}
+            "sample": "rows 0..%d of C (%d x %d x %d, %.1f s)" % (rows - 1, rows, wl.N, wl.K, secs),
+            "cpu_model": cpu_model(),
+            "one_thread_fp16_1024": {"seconds": round(one, 3),
+                                     "tflops": round(2.0 * 1024 ** 3 / one / 1e12, 5)}}
 
 
 def main():
@@ -278,6 +334,10 @@ def main():
                 del a, b, da, db, c
                 torch.cuda.empty_cache()
 
+    cold = None if args.no_table else cold_launches(tdg, si.WORKLOADS["fp16_skinny"])
+    if cold:
+        print("# cold (512 MiB scrub before each launch) %s" % json.dumps(cold), file=sys.stderr,
+              flush=True)
     ladder = None if args.no_ladder else transpose_ladder(tdg)
     ceilings = {} if args.no_ceilings else measured_ceilings(tdg, ladder)
 
@@ -331,6 +391,7 @@ def main():
                      "frac_of_measured": round(achieved / measured, 4) if measured else None},
         "measured_ceilings": ceilings,
         "launches": launches,
+        "cold": cold,
         "cpu_baseline": cpu,
         "variants": table or None,
         "transpose_ladder": ladder,

@@ -104,7 +104,20 @@ typedef struct {
  *   grid      -- workgroups launched, ceil(M/BM) * ceil(N/BN);
  *   est_regs  -- estimated 32-bit registers per lane for accumulators plus
  *                register staging;
- *   guarded   -- 1 when the shape or alignment needs the bounds-checked form. */
+ *   guarded   -- 1 when the shape or alignment needs the bounds-checked form;
+ *   need_bytes_per_clk -- bytes per clock per compute unit that must move
+ *                from L2 into LDS to keep the matrix cores busy: the CU's
+ *                MFMA operations per clock (4096 FP16, 8192 INT8, 256 FP32)
+ *                divided by `ratio`;
+ *   mfma_per_load -- instruction-count form of the ratio: MFMA instructions
+ *                per tile over 16-byte-per-lane wave load instructions per
+ *                tile ("Analyze Kernel Bottleneck", Step 4 counts compute and
+ *                load instructions per tile);
+ *   pipelined -- 1 when the chosen loop overlaps the load of tile t+1 with
+ *                compute on tile t; 0 for the sequential form, and for
+ *                num_tiles < 2, where the planner chooses the sequential
+ *                form ("Pipeline GPU Kernel", Step 1: pipelining needs at
+ *                least two K tiles). */
 typedef struct {
     double ratio;
     int band;
@@ -114,6 +127,9 @@ typedef struct {
     int64_t grid;
     int est_regs;
     int guarded;
+    double need_bytes_per_clk;
+    double mfma_per_load;
+    int pipelined;
 } tdg_plan_info;
 
 /* Sequential (single-buffer) baseline, FP16 -> FP32. */

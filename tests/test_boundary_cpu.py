@@ -184,6 +184,32 @@ def test_occupancy_limits_follow_the_160k_lds():
     assert tdg.tdg_tile_figures(tdg.TDG_DTYPE_I8I32, 128, 88, 256, stages=1)["wg_per_cu"] == 2
 
 
+def test_needed_bandwidth_and_instruction_ratio():
+    """The planner's MI355X figures: L2->LDS bytes per clock per CU that keep
+    the MFMAs busy (MFMA ops/clock/CU over the ratio) and MFMA instructions
+    per 16-byte wave load instruction."""
+    f16 = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 256, 256, 64, 8, 2, 3)
+    assert f16["ratio"] == 128.0 and f16["need_bytes_per_clk"] == 32.0
+    assert f16["mfma_per_load"] == 256 / 64          # 256 MFMAs, 64 KiB of loads
+    i8 = tdg.tdg_tile_figures(tdg.TDG_DTYPE_I8I32, 256, 256, 128, 8, 2, 3)
+    assert i8["ratio"] == 256.0 and i8["need_bytes_per_clk"] == 32.0 and i8["mfma_per_load"] == 4.0
+    f32 = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F32F32, 256, 256, 32, 8, 2, 3)
+    assert f32["ratio"] == 64.0 and f32["need_bytes_per_clk"] == 4.0 and f32["mfma_per_load"] == 16.0
+    skinny = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 64, 64, 64, 4, 4, 3)
+    assert skinny["ratio"] == 32.0 and skinny["need_bytes_per_clk"] == 128.0
+
+
+def test_one_k_tile_is_not_pipelined():
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4096, 4096, 4096)
+    assert info["pipelined"] == 1
+    for K in (1, 64):
+        cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4096, 4096, K)
+        assert cfg["variant"] == tdg.TDG_VARIANT_SINGLE and info["pipelined"] == 0
+        assert info["num_tiles"] == 1
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4096, 4096, 65)
+    assert info["num_tiles"] == 2 and info["pipelined"] == 1
+
+
 def test_grid_and_trip_count():
     info = tdg.tdg_tile_figures(tdg.TDG_DTYPE_F16F32, 256, 256, 64, 8, 2, 3, 4096, 4096, 4100)
     assert info["grid"] == 256 and info["num_tiles"] == 65
@@ -199,7 +225,7 @@ def test_planner_choices():
     assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH
     # ragged, but N and K whole 16-byte chunks: the copy stays in the DMA
     for code, M, N, K in [(0, 300, 264, 200), (0, 4000, 4000, 4000), (1, 300, 272, 144),
-                          (0, 16383, 64, 8192), (1, 1, 16, 16)]:
+                          (0, 16383, 64, 8192), (1, 1, 16, 272)]:
         cfg, info = tdg.tdg_plan(code, M, N, K)
         assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS, (M, N, K)
     # a K or N that splits a 16-byte chunk keeps the element-wise guarded loads

@@ -60,7 +60,9 @@ class TdgConfig(ctypes.Structure):
 class TdgPlanInfo(ctypes.Structure):
     _fields_ = [("ratio", ctypes.c_double), ("band", ctypes.c_int), ("lds_bytes", ctypes.c_size_t),
                 ("wg_per_cu", ctypes.c_int), ("num_tiles", ctypes.c_int64),
-                ("grid", ctypes.c_int64), ("est_regs", ctypes.c_int), ("guarded", ctypes.c_int)]
+                ("grid", ctypes.c_int64), ("est_regs", ctypes.c_int), ("guarded", ctypes.c_int),
+                ("need_bytes_per_clk", ctypes.c_double), ("mfma_per_load", ctypes.c_double),
+                ("pipelined", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -186,6 +186,17 @@ void tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int 
     info->grid = ceil_div(M, bm) * ceil_div(N, bn);
     info->est_regs = regs;
     info->guarded = 0;
+    // MI355X MFMA operations per clock per CU (dense peak / 256 CUs / 2.4 GHz)
+    const double ops_per_clk = dtype == TDG_DTYPE_F16F32 ? 4096.0
+                               : dtype == TDG_DTYPE_I8I32 ? 8192.0
+                                                          : 256.0;
+    info->need_bytes_per_clk = ops_per_clk / info->ratio;
+    // one 32x32 MFMA covers k = 16 (FP16), 32 (INT8) or 2 (FP32)
+    const double k_mfma = dtype == TDG_DTYPE_F16F32 ? 16.0 : dtype == TDG_DTYPE_I8I32 ? 32.0 : 2.0;
+    const double mfmas = (double)bm * bn * bk / (32.0 * 32.0 * k_mfma);
+    const double loads = bytes / 1024.0;  // 64 lanes x 16 bytes per wave instruction
+    info->mfma_per_load = mfmas / loads;
+    info->pipelined = variant != TDG_VARIANT_SINGLE && info->num_tiles >= 2;
 }
 
 void fill_info(const KernelEntry &e, int variant, int stages, int64_t M, int64_t N, int64_t K,
@@ -293,8 +304,12 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const bool edge = !fast && edge_ok(*tile, N, K, vec_ok);
 
     int variant = req.variant;
+    // With one K tile there is nothing to overlap ("Pipeline GPU Kernel",
+    // Step 1: pipelining needs at least two tiles); the planner then runs
+    // the sequential form, which computes the same result.
+    const bool one_tile = ceil_div(K, cfg_bk(*tile)) < 2;
     if (variant == TDG_VARIANT_AUTO)
-        variant = pipelined_default
+        variant = pipelined_default && !one_tile
                       ? (fast || edge ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
                       : TDG_VARIANT_SINGLE;
     int stages = req.lds_stages;
