@@ -33,6 +33,10 @@
  *   M, N, K >= 0;  lda >= max(1, K);  ldb >= max(1, N);  ldc >= max(1, N);
  *   a pointer may be NULL only when its matrix is empty;
  *   the bytes C spans may not overlap those of A or B.
+ * Leading dimensions must also satisfy 64 * ld * sizeof(T) + 256 < 2^31 for
+ * A and B (the kernels address 64 rows with 32-bit per-lane offsets): about
+ * 16 million FP16, 32 million INT8 or 8 million FP32 elements.  Larger ones
+ * return TDG_ERR_UNSUPPORTED.
  * Degenerate shapes: M == 0 or N == 0 returns TDG_OK and launches nothing;
  * K == 0 writes zeros to C.
  * Any shape and alignment is accepted.  The fast path needs 16-byte aligned

@@ -120,6 +120,15 @@ def test_mfma_probe_arguments():
     assert tdg.tdg_mfma_probe_sink_floats() == 512 * 256
 
 
+def test_oversized_leading_dimension_is_unsupported():
+    # 64 rows x lda x 2 bytes must stay below 2^31: lda = 2^24 is just over
+    lda = 1 << 24
+    assert tdg.call_raw("gemm_f16f32_pipelined", 64, 64, 64, 1 << 30, lda, 1 << 40, 64,
+                        1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
+    assert tdg.call_raw("gemm_i8i32", 64, 64, 64, 1 << 30, 64, 1 << 40, 1 << 25,
+                        1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
+
+
 def test_unbuilt_configuration_is_unsupported():
     cfg = tdg.TdgConfig(bm=96, bn=96, bk=0, waves=0, lds_stages=0, variant=0)
     with pytest.raises(tdg.TdgError) as e:

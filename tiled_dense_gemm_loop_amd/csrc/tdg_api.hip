@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "tdg_internal.h"
 #include "tdg_kernels.hpp"
@@ -16,22 +17,21 @@
 
 namespace tdg {
 
-// Both dtype tables, concatenated once.
+// The three dtype tables, concatenated once.
 const KernelEntry *kernel_table(int *count) {
-    static KernelEntry all[256];
-    static int n = 0;
+    static std::vector<KernelEntry> all;
     static std::once_flag once;
     std::call_once(once, [] {
         int nf = 0, ni = 0, n32 = 0;
         const KernelEntry *f = kernel_table_f16(&nf);
         const KernelEntry *i = kernel_table_i8(&ni);
         const KernelEntry *w = kernel_table_f32(&n32);
-        for (int k = 0; k < nf && n < 256; k++) all[n++] = f[k];
-        for (int k = 0; k < ni && n < 256; k++) all[n++] = i[k];
-        for (int k = 0; k < n32 && n < 256; k++) all[n++] = w[k];
+        all.insert(all.end(), f, f + nf);
+        all.insert(all.end(), i, i + ni);
+        all.insert(all.end(), w, w + n32);
     });
-    *count = n;
-    return all;
+    *count = (int)all.size();
+    return all.data();
 }
 
 // Whether the current device is gfx950 (cached per device).
