@@ -139,6 +139,32 @@ def time_launches(run, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
+def graph_launches(run, per_graph: int = 20, replays: int = 20) -> float:
+    """Mean milliseconds per launch when `per_graph` launches are captured in
+    one HIP graph and the graph is replayed: the launch-bound small shapes
+    then pay the graph's replay cost instead of one host call per launch."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm the library's caches outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (replays * per_graph)
+
+
 def individual_launches(run, count: int = 50) -> dict:
     """Median / min / max microseconds of `count` launches, each bracketed by
     its own pair of events on the launching stream."""
@@ -328,6 +354,12 @@ def main():
                 tp, bw = throughput(w, t)
                 row[variant] = {"us": round(t * 1e3, 2), "tops": round(tp, 1), "gbs": round(bw, 1)}
             row["speedup_pipelined_vs_single"] = round(row["single"]["us"] / row["pipelined"]["us"], 3)
+            if w.M * w.N * w.K <= 1024 ** 3:
+                # launch-bound shapes: the same launches replayed from a HIP graph
+                t = graph_launches(launcher(tdg, w, da, db, c, "pipelined"))
+                tp, bw = throughput(w, t)
+                row["pipelined_graph"] = {"us": round(t * 1e3, 2), "tops": round(tp, 1),
+                                          "gbs": round(bw, 1)}
             table[name] = row
             print("# %-12s %s" % (name, json.dumps(row)), file=sys.stderr, flush=True)
             if name != wl.name:

@@ -434,3 +434,32 @@ def test_large_ragged_sampled(lib, dtype, M, N, K):
     assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
     del C, dA, dB
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_graph_capture_replays(lib, dtype):
+    """The pipelined entry point captured in a HIP graph: every replay, with
+    new operand values copied in between, matches the oracle and the eager
+    call."""
+    import torch
+    M, N, K = 512, 384, 320
+    dA = to_device(_operands(dtype, M, N, K, seed=50)[0])
+    dB = to_device(_operands(dtype, M, N, K, seed=50)[1])
+    out_t = torch.int32 if dtype == I8 else torch.float32
+    C = torch.zeros((M, N), dtype=out_t, device="cuda")
+    gemm(lib, dtype, "pipelined", dA, dB, C)   # first call outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gemm(lib, dtype, "pipelined", dA, dB, C)
+    for rep in range(3):
+        A, B = _operands(dtype, M, N, K, seed=60 + rep)
+        dA.copy_(to_device(A))
+        dB.copy_(to_device(B))
+        C.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _check(dtype, C, A, B)
+        eager = gemm(lib, dtype, "pipelined", dA, dB)
+        assert torch.equal(C, eager)

@@ -138,6 +138,17 @@ def status_string(status: int) -> str:
 
 # ------------------------------------------------------------------ raw calls
 
+_FNS = {}
+
+
+def _fn(name: str):
+    """The library's entry point `name` (looked up once)."""
+    f = _FNS.get(name)
+    if f is None:
+        f = _FNS[name] = getattr(load_library(), name)
+    return f
+
+
 def call_raw(name: str, M, N, K, a_ptr, lda, b_ptr, ldb, c_ptr, ldc, stream=0, cfg=None) -> int:
     """Call a GEMM entry point with raw device pointers; returns the status."""
     fn = getattr(load_library(), name)
@@ -189,9 +200,16 @@ def _gemm(name, A, B, C, cfg, f16):
     Mc, Nc, pc, ldc = _matrix(C, (out_type,), "C")
     if (Mc, Nc) != (M, N):
         raise ValueError("C has shape %s, expected %s" % ((Mc, Nc), (M, N)))
-    with torch.cuda.device(A.device):
-        stream = torch.cuda.current_stream(A.device).cuda_stream
-        rc = call_raw(name, M, N, K, pa, lda, pb, ldb, pc, ldc, stream, cfg)
+    fn = _fn(name)
+    tail = (ctypes.byref(cfg) if cfg is not None else None,) if name.endswith("_ex") else ()
+    dev = A.device.index
+    if dev is None or dev == torch.cuda.current_device():
+        stream = torch.cuda.current_stream().cuda_stream
+        rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, stream, *tail)
+    else:
+        with torch.cuda.device(A.device):
+            stream = torch.cuda.current_stream(A.device).cuda_stream
+            rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, stream, *tail)
     if rc != TDG_OK:
         raise TdgError(rc, name)
     return C

@@ -207,13 +207,15 @@ void fill_info(const KernelEntry &e, int variant, int stages, int64_t M, int64_t
 }
 
 // Wave count and ring depth per tile shape that measured fastest for the
-// direct-to-LDS loop on MI355X (4096^3 FP16 and INT8, 16384 x 64 x 8192 FP16);
+// direct-to-LDS loop on MI355X (4096^3 FP16 and INT8, 2048^3 FP16,
+// 16384 x 64 x 8192 FP16);
 // tiles not listed use 4 waves and a two-buffer ring.
 struct Measured {
     int bm, bn, bkb, waves, stages;
 };
 const Measured kMeasured[] = {
     {256, 256, 128, 8, 2},
+    {128, 128, 128, 4, 4},  // FP16 2048^3: 24.6 us with 4 buffers, 26.4 with 2
     {128, 64, 128, 4, 4},
     {64, 64, 128, 4, 4},
 };
@@ -376,6 +378,62 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     return TDG_OK;
 }
 
+// Recent resolutions, so that repeated calls on one shape skip the table
+// scans.  The key holds everything resolve() reads: the request, the shape and
+// the two properties of the operands it looks at (alignment and whether the
+// leading dimensions fit the 32-bit per-lane offsets).
+struct PlanKey {
+    int dtype, variant_req, bm, bn, bk, waves, stages, pipelined_default, vec_ok, fits;
+    int64_t M, N, K;
+    bool operator==(const PlanKey &o) const { return memcmp(this, &o, sizeof(PlanKey)) == 0; }
+};
+struct PlanSlot {
+    bool used;
+    PlanKey key;
+    int rc;
+    Resolved r;
+};
+std::mutex g_plan_mutex;
+PlanSlot g_plans[16];
+unsigned g_plan_next = 0;
+
+int resolve_cached(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                   const void *B, int64_t ldb, const tdg_config &req, bool pipelined_default,
+                   Resolved *out) {
+    PlanKey key;
+    memset(&key, 0, sizeof(key));  // padding too: the key is compared bytewise
+    key.dtype = dtype;
+    key.variant_req = req.variant;
+    key.bm = req.bm;
+    key.bn = req.bn;
+    key.bk = req.bk;
+    key.waves = req.waves;
+    key.stages = req.lds_stages;
+    key.pipelined_default = pipelined_default ? 1 : 0;
+    key.vec_ok = aligned_operands(dtype, A, lda, B, ldb) ? 1 : 0;
+    key.fits = offsets_fit(dtype, lda, ldb) ? 1 : 0;
+    key.M = M;
+    key.N = N;
+    key.K = K;
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        for (const PlanSlot &slot : g_plans)
+            if (slot.used && slot.key == key) {
+                *out = slot.r;
+                return slot.rc;
+            }
+    }
+    const int rc = resolve(dtype, M, N, K, A, lda, B, ldb, req, pipelined_default, out, nullptr,
+                           nullptr);
+    std::lock_guard<std::mutex> lock(g_plan_mutex);
+    PlanSlot &slot = g_plans[g_plan_next++ % 16];
+    slot.used = true;
+    slot.key = key;
+    slot.rc = rc;
+    slot.r = *out;
+    return rc;
+}
+
 int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
         int64_t ldb, void *C, int64_t ldc, void *stream, const tdg_config *cfg,
         bool pipelined_default) {
@@ -386,7 +444,8 @@ int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, 
     memset(&req, 0, sizeof(req));
     if (cfg) req = *cfg;
     Resolved r;
-    rc = resolve(dtype, M, N, K, A, lda, B, ldb, req, pipelined_default, &r, nullptr, nullptr);
+    memset(&r, 0, sizeof(r));
+    rc = resolve_cached(dtype, M, N, K, A, lda, B, ldb, req, pipelined_default, &r);
     if (rc != TDG_OK) return rc;
     rc = device_check();
     if (rc != TDG_OK) return rc;
