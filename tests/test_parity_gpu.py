@@ -463,3 +463,46 @@ def test_graph_capture_replays(lib, dtype):
         _check(dtype, C, A, B)
         eager = gemm(lib, dtype, "pipelined", dA, dB)
         assert torch.equal(C, eager)
+
+
+# --- maximum sizes ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [131071, 131056])
+def test_int8_largest_k_without_overflow(lib, K):
+    """All inputs -128: C = 16384 * K, the largest INT32 sum the method can
+    produce at this K (131071 is the last K below 2^31 / 2^14).  K = 131071
+    runs the element-wise guarded loop, 131056 (whole 16-byte chunks) the
+    bounds-checked direct-to-LDS loop."""
+    import torch
+    M, N = 64, 80
+    A = np.full((M, K), -128, dtype=np.int8)
+    B = np.full((K, N), -128, dtype=np.int8)
+    for kind in ("single", "pipelined"):
+        C = gemm(lib, I8, kind, to_device(A), to_device(B))
+        assert torch.all(C == 16384 * K), kind
+    assert 16384 * 131071 < 2 ** 31
+
+
+def test_fp16_long_k_exact(lib):
+    """K = 131072 with +-1 inputs: every partial sum is an integer below 2^24,
+    so FP32 accumulation is exact in any order; the oracle decides."""
+    M, N, K = 64, 64, 131072
+    rng = np.random.default_rng(77)
+    A = np.where(rng.random((M, K)) < 0.5, np.float16(-1.0), np.float16(1.0)).astype(np.float16)
+    B = np.where(rng.random((K, N)) < 0.5, np.float16(-1.0), np.float16(1.0)).astype(np.float16)
+    A, B = A.view(np.uint16), B.view(np.uint16)
+    for kind in ("single", "pipelined"):
+        check_f16(gemm(lib, F16, kind, to_device(A), to_device(B)), A, B, exact=True)
+
+
+def test_tall_grid(lib):
+    """M = 2^20 rows, N = 64: 16384 workgroups; sampled rows against the
+    oracle, the whole output against the sequential loop."""
+    import torch
+    M, N, K = 1 << 20, 64, 128
+    A, B = _operands(F16, M, N, K, seed=88)
+    dA, dB = to_device(A), to_device(B)
+    C = gemm(lib, F16, "pipelined", dA, dB)
+    rows, cols = sample_indices(M, N, 4000, seed=88, tile_m=64, tile_n=64)
+    check_sampled(C, F16, A, B, rows, cols)
+    assert torch.equal(C, gemm(lib, F16, "single", dA, dB))
