@@ -22,14 +22,20 @@
 // loads write buffer (t + 1) % S, the epilogue computes buffer
 // (num_tiles - 1) % S.
 //
+// GUARD builds the bounds-checked form of each loop (ragged shapes): the
+// sequential and register loops load element by element with zero fill; the
+// direct-to-LDS loop fetches out-of-range 16-byte chunks from a zero block.
+//
 // Tile micro-kernel: each wave owns a (BM/WM) x (BN/WN) block of C held in
-// 32x32 MFMA accumulators (v_mfma_f32_32x32x16_f16 / v_mfma_i32_32x32x32_i8).
-// The K tile is BKB bytes of every row (64 FP16 or 128 INT8 elements at
+// 32x32 MFMA accumulators (v_mfma_f32_32x32x16_f16, v_mfma_i32_32x32x32_i8,
+// or four v_mfma_f32_32x32x2_f32 per K step for FP32 inputs).  The K tile is
+// BKB bytes of every row (64 FP16, 128 INT8 or 32 FP32 elements at
 // BKB = 128).  A is kept in LDS row-major (K contiguous) and read with
 // ds_read_b128; B is kept in LDS as it sits in memory (N contiguous) and read
 // with gfx950's transposing ds_read_b64_tr_b16 / ds_read_b64_tr_b8, which
-// hands each lane the K-contiguous column slice the MFMA B operand wants.
-// Both LDS images use 16-byte-chunk XOR swizzles chosen for gfx950's 64 banks
+// hands each lane the K-contiguous column slice the MFMA B operand wants
+// (FP32, for which no transposing read exists, takes four ds_read_b32).
+// The LDS images use 16-byte-chunk XOR swizzles chosen for gfx950's 64 banks
 // (256 bytes per cycle), so that the fragment reads, the register drains and
 // the DMA writes are free of bank conflicts.
 #pragma once
