@@ -45,9 +45,11 @@
  * multiples of 16 bytes (8 FP16 or 16 INT8 elements) keeps the direct-to-LDS
  * copy: chunks outside A or B are fetched from a zero block and stores are
  * masked.  Anything else runs the bounds-checked register-prefetch form of
- * the same kernel, which zero-fills out-of-range loads element by element
+ * the same kernel: one 16-byte load per chunk at any byte alignment, with
+ * rows outside the operand read from a zero block and K tails zeroed
  * ("Pipeline GPU Kernel", Common Pitfalls: boundary handling with async
- * copies).
+ * copies).  No load reaches past the 4 KiB page of a byte of A or B, so the
+ * operands need no padding.
  * Errors: TDG_ERR_NO_DEVICE when the current device is not gfx950 or no
  * device is present; TDG_ERR_UNSUPPORTED for an explicit configuration that is
  * not built in or does not fit the device; TDG_ERR_LAUNCH when the launch

@@ -237,7 +237,7 @@ def test_planner_choices():
                           (0, 16383, 64, 8192), (1, 1, 16, 272)]:
         cfg, info = tdg.tdg_plan(code, M, N, K)
         assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS, (M, N, K)
-    # a K or N that splits a 16-byte chunk keeps the element-wise guarded loads
+    # a K or N that splits a 16-byte chunk takes the guarded register-prefetch loop
     for code, M, N, K in [(0, 300, 264, 201), (0, 300, 260, 200), (1, 300, 272, 136)]:
         cfg, info = tdg.tdg_plan(code, M, N, K)
         assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH, (M, N, K)

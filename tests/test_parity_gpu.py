@@ -258,6 +258,48 @@ def test_strided_and_misaligned_operands(lib, dtype):
             _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
 
 
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_every_byte_alignment(lib, dtype):
+    """Odd leading dimensions, so rows start at every element offset within
+    a 16-byte chunk, and every base offset within a chunk; K and N split a
+    chunk, so the tails end at every position.  Whole chunks take the single
+    unaligned load, partial ones the shifted pair of aligned loads."""
+    epc = 16 // {F16: 2, I8: 1, F32: 4}[dtype]
+    M, N, K = 70, 46, 262                     # K, N even; both split a chunk
+    bigA, bigB = _operands(dtype, M + 1, N + 2 * epc + 1, K + 2 * epc + 1, seed=17)
+    dBigA, dBigB = to_device(bigA), to_device(bigB)
+    assert bigA.shape[1] % 2 == 1 and bigB.shape[1] % 2 == 1
+    for off in range(epc):
+        A = bigA[1:1 + M, off:off + K]
+        B = bigB[1:1 + K, epc - 1 - off:epc - 1 - off + N]
+        dA = dBigA[1:1 + M, off:off + K]
+        dB = dBigB[1:1 + K, epc - 1 - off:epc - 1 - off + N]
+        for kind in ("single", "pipelined"):
+            _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_tails_at_every_page_offset(lib, dtype):
+    """Odd leading dimensions over enough rows put the partial K
+    chunks of A and the partial N chunks of B at every element offset within
+    a 4 KiB page, so some of them would run past their page: those take the
+    pair of aligned loads instead of the single unaligned one."""
+    M, N, K = (4200, 46, 4202) if dtype == I8 else (2100, 46, 2102)   # rows cover every offset
+    bigA, bigB = _operands(dtype, M, N + 17, K + 1, seed=23)      # lda = K+1, ldb = N+17: odd
+    A, B = bigA[:, :K], bigB[:K, :N]
+    dBigA, dBigB = to_device(bigA), to_device(bigB)
+    dA, dB = dBigA[:, :K], dBigB[:K, :N]
+    esize = dA.element_size()
+    epc = 16 // esize
+    assert K % epc and N % epc
+    # page offsets of the first byte of each row's partial chunk
+    offs_a = {(dA.data_ptr() + (r * (K + 1) + K // epc * epc) * esize) % 4096 for r in range(M)}
+    offs_b = {(dB.data_ptr() + (r * (N + 17) + N // epc * epc) * esize) % 4096 for r in range(K)}
+    assert max(offs_a) > 4096 - 16 and max(offs_b) > 4096 - 16
+    for kind in ("single", "pipelined"):
+        _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
+
+
 def test_output_leading_dimension(lib):
     import torch
     M, N, K = 256, 256, 192
@@ -412,6 +454,28 @@ def test_full_size_sampled(lib, name):
     for vname, cfg in _variants(lib, dtype, tile):
         assert torch.equal(C_pipe, gemm(lib, dtype, "ex", dA, dB, cfg=cfg)), vname
     del C_pipe, C_single, dA, dB
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [(F16, 4095, 4095, 4095), (I8, 4097, 4097, 4097),
+                                         (F32, 4095, 4095, 4095)])
+def test_large_odd_sampled(lib, dtype, M, N, K):
+    """Odd sizes near the benchmark sizes: most rows start off a 16-byte
+    boundary, so the planner takes the guarded register-prefetch loop;
+    sampled elements (tile edges included) against the oracle, and the whole
+    output against the guarded sequential loop."""
+    import torch
+    A, B = _operands(dtype, M, N, K, seed=M + 7)
+    dA, dB = to_device(A), to_device(B)
+    code = CODE[dtype]
+    cfg, info = lib.tdg_plan(code, M, N, K)
+    assert info["guarded"] == 1 and cfg["variant"] == lib.TDG_VARIANT_REG_PREFETCH
+    rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=cfg["bn"])
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    check_sampled(C, dtype, A, B, rows, cols)
+    single = dict(cfg, variant=lib.TDG_VARIANT_SINGLE, lds_stages=1)
+    assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=single))
+    del C, dA, dB
     torch.cuda.empty_cache()
 
 

@@ -464,7 +464,6 @@ int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, 
     args.tiles_m = (int)ceil_div(M, e.bm);
     args.tiles_n = (int)ceil_div(N, e.bn);
     args.k_tiles = (int)ceil_div(K, cfg_bk(e));
-    args.vec_ok = aligned_operands(dtype, A, lda, B, ldb) ? 1 : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
     if (grid > INT32_MAX) return TDG_ERR_UNSUPPORTED;
 

@@ -23,8 +23,10 @@
 // (num_tiles - 1) % S.
 //
 // GUARD builds the bounds-checked form of each loop (ragged shapes): the
-// sequential and register loops load element by element with zero fill; the
-// direct-to-LDS loop fetches out-of-range 16-byte chunks from a zero block.
+// sequential and register loops check only the edge tiles, with one 16-byte
+// load per chunk at any alignment and a correction of partial chunks after
+// they land; the direct-to-LDS loop fetches out-of-range 16-byte chunks from
+// a zero block.
 //
 // Tile micro-kernel: each wave owns a (BM/WM) x (BN/WN) block of C held in
 // 32x32 MFMA accumulators (v_mfma_f32_32x32x16_f16, v_mfma_i32_32x32x32_i8,
@@ -52,6 +54,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_ua __attribute__((ext_vector_type(4), aligned(1)));  // any byte alignment
 
 #define TDG_LDS __attribute__((address_space(3)))
 #define TDG_GLOBAL __attribute__((address_space(1)))
@@ -68,7 +71,6 @@ struct GemmArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int k_tiles;  // ceil(K / BK); 0 when K == 0 (C is then zero-filled)
-    int vec_ok;   // 1 when every full 16-byte chunk of A and B is 16-byte aligned
 };
 
 // Compile-time geometry of one configuration.
@@ -241,25 +243,73 @@ __device__ static __forceinline__ void map_tile(int bid, int tiles_m, int tiles_
     tn = r / gm;
 }
 
-// One 16-byte chunk, bounds-checked: elements at and beyond `valid` (and all
-// elements when `row_ok` is false) read as zero; `vec` allows one 16-byte
-// load when the whole chunk is valid.
-template <int ES>
-__device__ static __forceinline__ u32x4 load_chunk_guarded(const unsigned char *p, bool row_ok,
-                                                           int valid, bool vec) {
+// A 16-byte load at any byte alignment from global memory.  The source is
+// chosen between an operand and the zero block, which would otherwise make it
+// a generic (flat) pointer, and flat loads also count against the LDS wait
+// counter.
+__device__ static __forceinline__ u32x4 load16_global(const unsigned char *p) {
+    return *(const __attribute__((address_space(1))) u32x4_ua *)p;
+}
+
+// One bounds-checked 16-byte chunk of a register-staged tile.  Rows outside
+// the operand (A rows >= M, B rows k >= K) and, with ZERO_TAIL, elements at
+// and beyond `valid` must read as zero: a k >= K would add to every sum.
+// Without ZERO_TAIL (B's columns >= N) the bytes past `valid` may hold
+// anything, because they only feed C columns that are never stored.
+// Every chunk is ONE 16-byte load, at any byte alignment: the HSA runtime
+// runs the chip in unaligned-access mode, and the compiler emits the same
+// instruction for a 16-byte load through a byte-aligned pointer.  Choosing
+// the source and correcting the loaded bytes are split, so that the loads of
+// a whole tile issue back to back and the correction runs after they have
+// landed, with no wait between them:
+//   * whole chunk: the load from p, no correction;
+//   * chunk outside the operand: the load from a zero block, no correction;
+//   * partial chunk (a K or N tail) whose 16 bytes stay in the 4 KiB page of
+//     p: the load from p, bytes past the valid ones zeroed afterwards when
+//     ZERO_TAIL;
+//   * partial chunk that would run past that page: the load of the 16 bytes
+//     that end with the last valid byte (they start within p's page), shifted
+//     down afterwards (and masked).
+// GPU memory is mapped in pages of 4 KiB or more, so every byte loaded lies
+// in a page that holds a valid byte.  `fix` returns the correction: 16 for
+// none, else the valid byte count plus the downward shift in bits 8 and up.
+template <int ES, bool ZERO_TAIL>
+__device__ static __forceinline__ const unsigned char *chunk_source(const unsigned char *p, bool row_ok,
+                                                                    int valid, uint32_t &fix) {
     constexpr int EPC = 16 / ES;
-    if (row_ok && vec && valid >= EPC) return *(const u32x4 *)p;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (row_ok) {
+    const bool any = row_ok && valid > 0;
+    const uint32_t nbytes = (uint32_t)valid * ES;  // < 16 when partial
+    const bool tail = any && valid < EPC;
+    const bool end_anchor = tail && ((uintptr_t)p & 4095) > 4096 - 16;
+    const uint32_t shift = end_anchor ? 16u - nbytes : 0u;
+    fix = tail && (ZERO_TAIL || end_anchor) ? (nbytes | shift << 8) : 16u;
+    return !any ? (const unsigned char *)tdg_zero16 : p - shift;
+}
+
+__device__ static __forceinline__ u32x4 chunk_fixup(u32x4 v, uint32_t fix) {
+    if (fix & 16u) return v;
+    uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+    const uint32_t shift = fix >> 8;
+    if (shift) {  // end-anchored chunk: move byte `shift` down to byte 0
+        const uint32_t d[8] = {w[0], w[1], w[2], w[3], 0u, 0u, 0u, 0u};
+        const uint32_t ds = shift >> 2, bs = shift & 3;
+        // e[j] = d[ds + j], selected without indexing a register array
+        uint32_t e[5];
 #pragma unroll
-        for (int e = 0; e < EPC; e++) {
-            if (e < valid) {
-                uint32_t v = ES == 4   ? ((const uint32_t *)p)[e]
-                             : ES == 2 ? (uint32_t)((const uint16_t *)p)[e]
-                                       : (uint32_t)p[e];
-                w[(e * ES) >> 2] |= v << (((e * ES) & 3) * 8);
-            }
+        for (int j = 0; j < 5; j++) {
+            const uint32_t x0 = d[j], x1 = d[j + 1], x2 = d[j + 2], x3 = d[j + 3];
+            e[j] = ds == 0 ? x0 : ds == 1 ? x1 : ds == 2 ? x2 : x3;
         }
+#pragma unroll
+        for (int j = 0; j < 4; j++) w[j] = __builtin_amdgcn_alignbyte(e[j + 1], e[j], bs);  // bytes bs.. of e[j]:e[j+1]
+    }
+    // keep bytes [0, nbytes): word j keeps min(max(nbytes - 4j, 0), 4) bytes
+    const int nbytes = (int)(fix & 15u);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int left = nbytes - 4 * j;
+        const uint32_t keep = left >= 4 ? 32u : (left > 0 ? 8u * (uint32_t)left : 0u);
+        w[j] &= (uint32_t)((1ull << keep) - 1ull);
     }
     return u32x4{w[0], w[1], w[2], w[3]};
 }
@@ -352,6 +402,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
 
     // ---- building blocks ---------------------------------------------------
     u32x4 ra[G::CA], rb[G::CB];  // register staging (SINGLE / REG)
+    uint32_t fix_a[G::CA], fix_b[G::CB];  // their corrections (GUARD)
 
     auto a_ptr = [&](int kt, int i) {
         return a_base + (int64_t)kt * G::BKB + (int64_t)(i * A_RSTEP) * lda_b;
@@ -366,28 +417,57 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
 #pragma unroll
             for (int i = 0; i < G::CB; i++) rb[i] = *(const u32x4 *)(b_ptr(kt, i) + b_voff);
         } else {
-            const bool vec = args.vec_ok != 0;
+            // Only the last K tile (when K is not a whole number of tiles)
+            // and the M or N edge tiles need the checks; the test is uniform
+            // over the workgroup, so interior tiles take plain sources.  All
+            // sources are chosen before the first load issues: address work
+            // between loads can make the compiler wait for the loads already
+            // in flight.
             const int kbase = kt * G::BK;
             constexpr int EPC = 16 / G::ES;
+            const bool k_inside = kbase + G::BK <= args.K;
+            const unsigned char *src_a[G::CA], *src_b[G::CB];
+            if (k_inside && m0 + G::BM <= args.M) {
 #pragma unroll
-            for (int i = 0; i < G::CA; i++) {
-                const bool row_ok = m0 + i * A_RSTEP + a_r0 < args.M;
-                const int valid = args.K - (kbase + a_c * EPC);
-                ra[i] = load_chunk_guarded<G::ES>(a_ptr(kt, i) + a_voff, row_ok, valid, vec);
+                for (int i = 0; i < G::CA; i++) {
+                    src_a[i] = a_ptr(kt, i) + a_voff;
+                    fix_a[i] = 16u;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < G::CA; i++) {
+                    const bool row_ok = m0 + i * A_RSTEP + a_r0 < args.M;
+                    const int valid = args.K - (kbase + a_c * EPC);
+                    src_a[i] = chunk_source<G::ES, true>(a_ptr(kt, i) + a_voff, row_ok, valid, fix_a[i]);
+                }
+            }
+            if (k_inside && n0 + G::BN <= args.N) {
+#pragma unroll
+                for (int i = 0; i < G::CB; i++) {
+                    src_b[i] = b_ptr(kt, i) + b_voff;
+                    fix_b[i] = 16u;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < G::CB; i++) {
+                    const bool row_ok = kbase + i * B_RSTEP + b_k0 < args.K;
+                    const int valid = args.N - (n0 + b_c * EPC);
+                    src_b[i] = chunk_source<G::ES, false>(b_ptr(kt, i) + b_voff, row_ok, valid, fix_b[i]);
+                }
             }
 #pragma unroll
-            for (int i = 0; i < G::CB; i++) {
-                const bool row_ok = kbase + i * B_RSTEP + b_k0 < args.K;
-                const int valid = args.N - (n0 + b_c * EPC);
-                rb[i] = load_chunk_guarded<G::ES>(b_ptr(kt, i) + b_voff, row_ok, valid, vec);
-            }
+            for (int i = 0; i < G::CA; i++) ra[i] = load16_global(src_a[i]);
+#pragma unroll
+            for (int i = 0; i < G::CB; i++) rb[i] = load16_global(src_b[i]);
         }
     };
     auto store_regs = [&](unsigned char *st) {
 #pragma unroll
-        for (int i = 0; i < G::CA; i++) lds_write16(st + slot + i * G::NT * 16, ra[i]);
+        for (int i = 0; i < G::CA; i++)
+            lds_write16(st + slot + i * G::NT * 16, GUARD ? chunk_fixup(ra[i], fix_a[i]) : ra[i]);
 #pragma unroll
-        for (int i = 0; i < G::CB; i++) lds_write16(st + G::A_BYTES + slot + i * G::NT * 16, rb[i]);
+        for (int i = 0; i < G::CB; i++)
+            lds_write16(st + G::A_BYTES + slot + i * G::NT * 16, GUARD ? chunk_fixup(rb[i], fix_b[i]) : rb[i]);
     };
     // LDS DMA: each lane's 16 bytes land at M0 + 16 * lane.  Issued from
     // inline assembly so that the compiler does not guard the other buffer's
@@ -634,6 +714,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
 
     // ---- C write-back: 32x32 accumulator layout -> row-major C -------------
     // lane l of block (mi, ni) holds rows 8*(v/4) + 4*(l/32) + v%4, column l%32.
+    // Every tile load has landed by now; saying so with a counted wait keeps
+    // the compiler from guarding the stores' address registers (once tile
+    // load destinations) with waits on the stores themselves.
+    wait_vmcnt<0>();
     out_t *C = (out_t *)args.C;
     const int col_l = lane & 31, rq = (lane >> 5) * 4;
 #pragma unroll
