@@ -194,6 +194,19 @@ int tdg_config_at(int dtype, int index, tdg_config *out);
 /* Human-readable name of a status code (static storage). */
 const char *tdg_status_string(int status);
 
+/* ---- Debugging aid: a race screen for the K-loop's buffer discipline
+ * ("Pipeline GPU Kernel", Common Pitfalls: a missing wait or barrier, or a
+ * wrong buffer index, lets compute read a tile that has not landed).  With
+ * TDG_DEBUG_POISON_LDS set, every GEMM launched afterwards first fills its
+ * whole LDS ring with 0xFF bytes, so such a read yields NaN (FP16, FP32) or
+ * -1 (INT8) and fails a comparison with the oracle, rather than passing on
+ * stale LDS contents.  Results of correct kernels are unchanged; the fill
+ * costs one pass over LDS per workgroup.  The setting is process-wide and
+ * read at launch (a graph captured earlier keeps its own).  Returns the
+ * previous flags; unknown bits are rejected with TDG_ERR_INVALID_ARG. */
+enum { TDG_DEBUG_POISON_LDS = 1 };
+int tdg_set_debug_flags(int flags);
+
 /* ---- Copy / transpose ladder ("fixing GPU kernels by hand", the transpose
  * exercise in four steps).  A rows x cols matrix of 32-bit elements (float;
  * the bits are moved, never computed on) is copied or transposed between

@@ -258,3 +258,13 @@ def test_planner_choices():
             c = tdg.tdg_config_at(code, i)
             got, _ = tdg.tdg_plan(code, 4 * c["bm"], 4 * c["bn"], 8 * c["bk"], dict(c))
             assert got == c
+
+
+def test_debug_flags_round_trip():
+    """The race-screen switch is host state: set, read back, reset; unknown
+    bits are rejected without changing the setting."""
+    assert tdg.tdg_set_debug_flags(tdg.TDG_DEBUG_POISON_LDS) == 0
+    with pytest.raises(tdg.TdgError):
+        tdg.tdg_set_debug_flags(2)
+    assert tdg.tdg_set_debug_flags(0) == tdg.TDG_DEBUG_POISON_LDS
+    assert tdg.tdg_set_debug_flags(0) == 0

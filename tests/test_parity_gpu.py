@@ -135,6 +135,35 @@ def test_tile_shape_all_variants(lib, dtype, tile):
             assert torch.equal(ref_out, C), "variant %s differs from single" % name
 
 
+@pytest.mark.parametrize("dtype,tile", _all_tiles(),
+                         ids=lambda v: v if isinstance(v, str) else
+                         "%dx%dx%d_w%d" % (v["bm"], v["bn"], v["bk"], v["waves"]))
+def test_poisoned_lds_race_screen(lib, dtype, tile):
+    """Every loop form with the LDS ring filled with 0xFF bytes before the
+    first tile lands: a read of a buffer the pipeline has not filled yet
+    would see NaN (FP16, FP32) or -1 (INT8).  Whole tiles, a chunk-aligned
+    ragged shape (bounds-checked direct-to-LDS) and a chunk-splitting one
+    (bounds-checked register loads); each against the oracle and bitwise
+    against the same launch without the poison."""
+    import torch
+    epc = 16 // {F16: 2, I8: 1, F32: 4}[dtype]
+    bm, bn, bk = tile["bm"], tile["bn"], tile["bk"]
+    shapes = [(2 * bm, 2 * bn, 3 * bk), (2 * bm - 3, 2 * bn - epc, 3 * bk - epc),
+              (2 * bm - 5, 2 * bn - 3, 3 * bk - 1)]
+    for si_, (M, N, K) in enumerate(shapes):
+        A, B = _operands(dtype, M, N, K, seed=7 * M + N + K + si_)
+        dA, dB = to_device(A), to_device(B)
+        for name, cfg in _variants(lib, dtype, tile):
+            clean = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+            prev = lib.tdg_set_debug_flags(lib.TDG_DEBUG_POISON_LDS)
+            try:
+                C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+            finally:
+                lib.tdg_set_debug_flags(prev)
+            _check(dtype, C, A, B)
+            assert torch.equal(C, clean), "%s at %s changes under poisoned LDS" % (name, (M, N, K))
+
+
 # --- ragged, tiny and degenerate shapes (bounds-checked path) ---------------------------
 
 RAGGED = [(1, 1, 1), (5, 7, 3), (64, 64, 1), (33, 65, 17), (300, 290, 333), (257, 129, 65),

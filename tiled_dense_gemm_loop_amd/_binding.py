@@ -27,6 +27,7 @@ TDG_VARIANT_AUTO = 0
 TDG_VARIANT_SINGLE = 1
 TDG_VARIANT_REG_PREFETCH = 2
 TDG_VARIANT_DIRECT_LDS = 3
+TDG_DEBUG_POISON_LDS = 1
 
 VARIANT_NAMES = {0: "auto", 1: "single", 2: "reg_prefetch", 3: "direct_lds"}
 
@@ -44,7 +45,7 @@ EXPORTED = (
     "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
     "gemm_f16f32_ex", "gemm_i8i32_ex", "gemm_f32f32", "gemm_f32f32_pipelined", "gemm_f32f32_ex",
     "tdg_plan", "tdg_tile_figures", "tdg_config_count",
-    "tdg_config_at", "tdg_status_string", "tdg_copy_f32", "tdg_transpose_f32",
+    "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
 )
 
@@ -118,6 +119,8 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_config_at.restype = c_int
     lib.tdg_status_string.argtypes = [c_int]
     lib.tdg_status_string.restype = ctypes.c_char_p
+    lib.tdg_set_debug_flags.argtypes = [c_int]
+    lib.tdg_set_debug_flags.restype = c_int
     lib.tdg_copy_f32.argtypes = [i64, i64, vp, i64, vp, i64, vp]
     lib.tdg_copy_f32.restype = c_int
     lib.tdg_transpose_f32.argtypes = [c_int, i64, i64, vp, i64, vp, i64, vp]
@@ -286,6 +289,14 @@ def tdg_tile_figures(dtype: int, bm: int, bn: int, bk: int, waves: int = 4, stag
     if rc != TDG_OK:
         raise TdgError(rc, "tdg_tile_figures")
     return info.as_dict()
+
+
+def tdg_set_debug_flags(flags: int) -> int:
+    """Sets the process-wide TDG_DEBUG_* bits; returns the previous ones."""
+    rc = load_library().tdg_set_debug_flags(flags)
+    if rc < 0:
+        raise TdgError(rc, "tdg_set_debug_flags")
+    return rc
 
 
 def tdg_config_count(dtype: int) -> int:

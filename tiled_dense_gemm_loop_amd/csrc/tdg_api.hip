@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -16,6 +17,9 @@
 #include "tdgemm.h"
 
 namespace tdg {
+
+// TDG_DEBUG_* bits passed to every GEMM launch (tdg_set_debug_flags).
+static std::atomic<int> debug_flags{0};
 
 // The three dtype tables, concatenated once.
 const KernelEntry *kernel_table(int *count) {
@@ -464,6 +468,7 @@ int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, 
     args.tiles_m = (int)ceil_div(M, e.bm);
     args.tiles_n = (int)ceil_div(N, e.bn);
     args.k_tiles = (int)ceil_div(K, cfg_bk(e));
+    args.flags = tdg::debug_flags.load(std::memory_order_relaxed);
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
     if (grid > INT32_MAX) return TDG_ERR_UNSUPPORTED;
 
@@ -585,6 +590,11 @@ int tdg_config_at(int dtype, int index, tdg_config *out) {
         n++;
     }
     return TDG_ERR_INVALID_ARG;
+}
+
+int tdg_set_debug_flags(int flags) {
+    if (flags & ~TDG_DEBUG_POISON_LDS) return TDG_ERR_INVALID_ARG;
+    return tdg::debug_flags.exchange(flags);
 }
 
 const char *tdg_status_string(int status) {

@@ -44,6 +44,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "tdgemm.h"
 
 namespace tdg {
 
@@ -71,6 +72,7 @@ struct GemmArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int k_tiles;  // ceil(K / BK); 0 when K == 0 (C is then zero-filled)
+    int flags;    // TDG_DEBUG_* bits
 };
 
 // Compile-time geometry of one configuration.
@@ -337,6 +339,17 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     map_tile(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nt = args.k_tiles;
+
+    // Race screen: with the debug flag set, the whole LDS ring is filled with
+    // 0xFF bytes before the first tile is requested.  A fragment read of a
+    // buffer that the pipeline has not filled yet then sees NaN (FP16, FP32)
+    // or -1 (INT8), and the result fails parity instead of passing on
+    // whatever an earlier kernel left in LDS.
+    if (args.flags & TDG_DEBUG_POISON_LDS) {
+        for (int o = tid * 16; o < STAGES * G::STAGE_BYTES; o += G::NT * 16)
+            lds_write16(smem + o, u32x4{~0u, ~0u, ~0u, ~0u});
+        __syncthreads();
+    }
 
     // Chunk i of this thread sits at LDS slot i*NT + tid of the A (or B)
     // image, i.e. image row i*RSTEP + tid/CPR and physical chunk tid % CPR.
