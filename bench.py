@@ -355,11 +355,17 @@ def main():
                 row[variant] = {"us": round(t * 1e3, 2), "tops": round(tp, 1), "gbs": round(bw, 1)}
             row["speedup_pipelined_vs_single"] = round(row["single"]["us"] / row["pipelined"]["us"], 3)
             if w.M * w.N * w.K <= 1024 ** 3:
-                # launch-bound shapes: the same launches replayed from a HIP graph
-                t = graph_launches(launcher(tdg, w, da, db, c, "pipelined"))
-                tp, bw = throughput(w, t)
-                row["pipelined_graph"] = {"us": round(t * 1e3, 2), "tops": round(tp, 1),
-                                          "gbs": round(bw, 1)}
+                # launch-bound shapes: every form again, replayed from a HIP graph,
+                # so that the comparison is between kernels, not host calls
+                graph = {}
+                for variant in ("single", "reg_s1", "reg_s2", "direct", "pipelined"):
+                    t = graph_launches(launcher(tdg, w, da, db, c, variant))
+                    tp, bw = throughput(w, t)
+                    graph[variant] = {"us": round(t * 1e3, 2), "tops": round(tp, 1),
+                                      "gbs": round(bw, 1)}
+                graph["speedup_pipelined_vs_single"] = round(
+                    graph["single"]["us"] / graph["pipelined"]["us"], 3)
+                row["graph"] = graph
             table[name] = row
             print("# %-12s %s" % (name, json.dumps(row)), file=sys.stderr, flush=True)
             if name != wl.name:
