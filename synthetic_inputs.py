@@ -42,6 +42,15 @@ def f16_integers(rows: int, cols: int, seed: int, lo: int = -8, hi: int = 8) -> 
     return rng.integers(lo, hi + 1, size=(rows, cols)).astype(np.float16).view(np.uint16)
 
 
+def f16_subnormals(rows: int, cols: int, seed: int) -> np.ndarray:
+    """binary16 subnormals: random sign, exponent field 0, mantissa field
+    uniform on [1, 1023], i.e. values m * 2^-24; returns uint16 bits."""
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, size=(rows, cols), dtype=np.uint16) << np.uint16(15)
+    mant = rng.integers(1, 1024, size=(rows, cols), dtype=np.uint16)
+    return sign | mant
+
+
 def f32_normal(rows: int, cols: int, seed: int) -> np.ndarray:
     """N(0, 1) float32 draws, shape (rows, cols)."""
     rng = np.random.default_rng(seed)

@@ -82,6 +82,22 @@ def test_brute_force_f16_exact_fractions(M, N, K):
 
 # --- exhaustive int8 product table ------------------------------------------------
 
+def test_subnormal_products_closed_form():
+    """Subnormal A (m * 2^-24, from its bit fields alone) times integer B:
+    C = (sum_k s_ik m_ik b_kj) * 2^-24 exactly, computed in int64 from the
+    sign and mantissa fields, with no binary16 decode at all."""
+    M, N, K = 37, 29, 300
+    A = si.f16_subnormals(M, K, seed=5)
+    B = si.f16_integers(K, N, seed=6)
+    sign = np.where(A >> 15, -1, 1).astype(np.int64)
+    m = (A & 0x3FF).astype(np.int64) * sign
+    b = B.view(np.float16).astype(np.int64)
+    want = (m @ b).astype(np.float64) * 2.0 ** -24
+    got, S = oracle.gemm_f16(A, B)
+    assert np.array_equal(got, want)
+    assert np.array_equal(S, (np.abs(m) @ np.abs(b)).astype(np.float64) * 2.0 ** -24)
+
+
 def test_exhaustive_int8_product_table():
     vals = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
     A = vals.reshape(256, 1).copy()

@@ -298,13 +298,20 @@ def test_every_byte_alignment(lib, dtype):
     bigA, bigB = _operands(dtype, M + 1, N + 2 * epc + 1, K + 2 * epc + 1, seed=17)
     dBigA, dBigB = to_device(bigA), to_device(bigB)
     assert bigA.shape[1] % 2 == 1 and bigB.shape[1] % 2 == 1
+    import torch
+    out_t = torch.int32 if dtype == I8 else torch.float32
     for off in range(epc):
         A = bigA[1:1 + M, off:off + K]
         B = bigB[1:1 + K, epc - 1 - off:epc - 1 - off + N]
         dA = dBigA[1:1 + M, off:off + K]
         dB = dBigB[1:1 + K, epc - 1 - off:epc - 1 - off + N]
         for kind in ("single", "pipelined"):
-            _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
+            # C at every 4-byte offset within 16 bytes too, with ldc = N + 5
+            co = off % 4
+            bigC = torch.full((M, N + 5), -3, dtype=out_t, device="cuda")
+            C = bigC[:, co:co + N]
+            _check(dtype, gemm(lib, dtype, kind, dA, dB, C), A, B)
+            assert torch.all(bigC[:, :co] == -3) and torch.all(bigC[:, co + N:] == -3)
 
 
 @pytest.mark.parametrize("dtype", [F16, I8, F32])
@@ -350,6 +357,25 @@ def test_integer_valued_fp16_is_exact(lib):
         dA, dB = to_device(A), to_device(B)
         for kind in ("single", "pipelined"):
             check_f16(gemm(lib, F16, kind, dA, dB), A, B, exact=True)
+
+
+@pytest.mark.parametrize("M,N,K,which", [(256, 192, 512, "A"), (192, 256, 512, "B"),
+                                          (130, 70, 16, "both")])
+def test_fp16_subnormal_inputs_are_exact(lib, M, N, K, which):
+    """binary16 subnormals (m * 2^-24) against small integers, or against each
+    other at small K: every product and partial sum is an integer multiple of
+    2^-24 (2^-48) below 2^24 units, so FP32 holds it exactly in any order and
+    the result must equal the oracle bit for bit.  A flush of subnormal
+    inputs to zero fails this."""
+    sub_a = which in ("A", "both")
+    sub_b = which in ("B", "both")
+    A = si.f16_subnormals(M, K, seed=M + K) if sub_a else si.f16_integers(M, K, seed=M + K)
+    B = si.f16_subnormals(K, N, seed=N + K) if sub_b else si.f16_integers(K, N, seed=N + K)
+    dA, dB = to_device(A), to_device(B)
+    for kind in ("single", "pipelined"):
+        C = gemm(lib, F16, kind, dA, dB)
+        check_f16(C, A, B, exact=True)
+        assert C.abs().max().item() > 0
 
 
 def test_integer_valued_fp32_is_exact(lib):
