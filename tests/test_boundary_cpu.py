@@ -268,3 +268,44 @@ def test_debug_flags_round_trip():
         tdg.tdg_set_debug_flags(2)
     assert tdg.tdg_set_debug_flags(0) == tdg.TDG_DEBUG_POISON_LDS
     assert tdg.tdg_set_debug_flags(0) == 0
+
+
+def test_concurrent_calls_resolve_consistently():
+    """Eight host threads resolve a churn of shapes and explicit configs at
+    once through the GEMM entry points (the plan cache holds 16 entries, so
+    slots are replaced while others read them).  Every status must equal the
+    one a single thread gets: TDG_ERR_NO_DEVICE for a plan that resolves (no
+    GPU here; resolution runs first) and TDG_ERR_UNSUPPORTED for a config
+    that is not built.  ctypes releases the GIL during each call."""
+    import random
+    import threading
+    bad = tdg.TdgConfig(96, 96, 64, 4, 2, tdg.TDG_VARIANT_DIRECT_LDS)   # not built
+    calls = []
+    rng = random.Random(3)
+    for _ in range(400):
+        M, N, K = rng.randint(1, 5000), rng.randint(1, 5000), rng.randint(1, 5000)
+        name = rng.choice(["gemm_f16f32_pipelined", "gemm_i8i32", "gemm_f32f32_ex",
+                           "gemm_i8i32_ex"])
+        cfg = bad if name.endswith("_ex") and rng.random() < 0.5 else (
+            tdg.TdgConfig() if name.endswith("_ex") else None)
+        # fake, 16-byte aligned, non-overlapping pointers: nothing is dereferenced
+        calls.append((name, M, N, K, 1 << 40, K, 2 << 40, N, 3 << 40, N, 0, cfg))
+    expected = [tdg.call_raw(*c) for c in calls]
+    assert set(expected) <= {tdg.TDG_ERR_NO_DEVICE, tdg.TDG_ERR_UNSUPPORTED}
+    assert tdg.TDG_ERR_UNSUPPORTED in expected and tdg.TDG_ERR_NO_DEVICE in expected
+    got = [[None] * len(calls) for _ in range(8)]
+
+    def worker(w):
+        order = list(range(len(calls)))
+        random.Random(w).shuffle(order)
+        for _ in range(3):
+            for i in order:
+                got[w][i] = tdg.call_raw(*calls[i])
+
+    threads = [threading.Thread(target=worker, args=(w,)) for w in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for w in range(8):
+        assert got[w] == expected, "thread %d disagrees" % w

@@ -472,6 +472,40 @@ def test_repeat_runs_are_bitwise_identical(lib):
         assert torch.equal(first, gemm(lib, F16, "pipelined", dA, dB))
 
 
+def test_concurrent_streams_from_host_threads(lib):
+    """Four host threads, each on a stream of its own, launch products of
+    different dtypes and shapes at the same time (the plan cache is shared);
+    every result matches the oracle and repeats bit for bit."""
+    import threading
+    import torch
+    cases = [(F16, 512, 384, 640), (I8, 300, 290, 333), (F32, 256, 320, 256), (F16, 1000, 70, 129)]
+    host = [_operands(dt, M, N, K, seed=40 + i) for i, (dt, M, N, K) in enumerate(cases)]
+    dev = [(to_device(A), to_device(B)) for A, B in host]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(cases), []
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                outs = [gemm(lib, cases[i][0], "pipelined", *dev[i]) for _ in range(6)]
+            stream.synchronize()
+            results[i] = outs
+        except Exception as exc:  # reported below, in the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for (dt, M, N, K), (A, B), outs in zip(cases, host, results):
+        _check(dt, outs[0], A, B)
+        for C in outs[1:]:
+            assert torch.equal(C, outs[0])
+
+
 def test_invalid_arguments_are_rejected(lib):
     import torch
     A = torch.zeros((64, 64), dtype=torch.int8, device="cuda")
