@@ -123,7 +123,13 @@ typedef struct {
  *                compute on tile t; 0 for the sequential form, and for
  *                num_tiles < 2, where the planner chooses the sequential
  *                form ("Pipeline GPU Kernel", Step 1: pipelining needs at
- *                least two K tiles). */
+ *                least two K tiles);
+ *   k_rotated -- 1 when each tile row walks its K tiles starting at its own
+ *                offset (tile row mod num_tiles).  Chosen when all of B fits
+ *                in half an XCD's L2 (K * N * sizeof(T) <= 2 MiB): B is then
+ *                read from L2 in any order, and the rotation spreads A's
+ *                concurrent reads over the HBM channels.  It changes the
+ *                FP32 summation order (per tile row), not the product. */
 typedef struct {
     double ratio;
     int band;
@@ -136,6 +142,7 @@ typedef struct {
     double need_bytes_per_clk;
     double mfma_per_load;
     int pipelined;
+    int k_rotated;
 } tdg_plan_info;
 
 /* Sequential (single-buffer) baseline, FP16 -> FP32. */
@@ -202,9 +209,11 @@ const char *tdg_status_string(int status);
  * -1 (INT8) and fails a comparison with the oracle, rather than passing on
  * stale LDS contents.  Results of correct kernels are unchanged; the fill
  * costs one pass over LDS per workgroup.  The setting is process-wide and
- * read at launch (a graph captured earlier keeps its own).  Returns the
- * previous flags; unknown bits are rejected with TDG_ERR_INVALID_ARG. */
-enum { TDG_DEBUG_POISON_LDS = 1 };
+ * read at launch (a graph captured earlier keeps its own).
+ * TDG_DEBUG_NO_K_ROTATION turns the K-tile rotation off (see k_rotated in
+ * tdg_plan_info), for comparing the two walks.  Returns the previous flags;
+ * unknown bits are rejected with TDG_ERR_INVALID_ARG. */
+enum { TDG_DEBUG_POISON_LDS = 1, TDG_DEBUG_NO_K_ROTATION = 2 };
 int tdg_set_debug_flags(int flags);
 
 /* ---- Copy / transpose ladder ("fixing GPU kernels by hand", the transpose

@@ -265,7 +265,7 @@ def test_debug_flags_round_trip():
     bits are rejected without changing the setting."""
     assert tdg.tdg_set_debug_flags(tdg.TDG_DEBUG_POISON_LDS) == 0
     with pytest.raises(tdg.TdgError):
-        tdg.tdg_set_debug_flags(2)
+        tdg.tdg_set_debug_flags(4)
     assert tdg.tdg_set_debug_flags(0) == tdg.TDG_DEBUG_POISON_LDS
     assert tdg.tdg_set_debug_flags(0) == 0
 
@@ -309,3 +309,19 @@ def test_concurrent_calls_resolve_consistently():
         t.join()
     for w in range(8):
         assert got[w] == expected, "thread %d disagrees" % w
+
+
+def test_k_rotation_rule():
+    """Tile rows walk K from their own offsets exactly when all of B fits in
+    2 MiB (half an XCD's L2)."""
+    cases = [((tdg.TDG_DTYPE_F16F32, 16384, 64, 8192), 1),      # B = 1 MiB
+             ((tdg.TDG_DTYPE_F16F32, 1024, 1024, 1024), 1),     # B = 2 MiB
+             ((tdg.TDG_DTYPE_F16F32, 1024, 1024, 1025), 0),
+             ((tdg.TDG_DTYPE_F16F32, 4096, 4096, 4096), 0),
+             ((tdg.TDG_DTYPE_I8I32, 4096, 4096, 4096), 0),
+             ((tdg.TDG_DTYPE_I8I32, 256, 256, 256), 1),
+             ((tdg.TDG_DTYPE_F32F32, 4096, 128, 4096), 1),      # B = 2 MiB
+             ((tdg.TDG_DTYPE_F32F32, 4096, 129, 4096), 0)]
+    for args, want in cases:
+        _, info = tdg.tdg_plan(*args)
+        assert info["k_rotated"] == want, args

@@ -506,6 +506,34 @@ def test_concurrent_streams_from_host_threads(lib):
             assert torch.equal(C, outs[0])
 
 
+@pytest.mark.parametrize("dtype,M,N,K", [(F16, 2048, 64, 8192), (I8, 2048, 64, 8192),
+                                         (F32, 1024, 64, 4096), (F16, 1000, 70, 4000),
+                                         (I8, 777, 100, 5000), (F16, 512, 512, 1024)])
+def test_k_rotation_against_the_plain_walk(lib, dtype, M, N, K):
+    """Shapes whose B fits in L2 walk K from a per-tile-row offset.  The
+    same call with the rotation switched off (debug flag) walks K from 0:
+    both match the oracle, INT8 bit for bit (and the sequential entry point
+    too), so only the summation order differs.  The loop forms' bitwise
+    agreement under the rotation is what test_tile_shape_all_variants checks
+    (its shapes all rotate)."""
+    import torch
+    _, info = lib.tdg_plan(CODE[dtype], M, N, K)
+    assert info["k_rotated"] == 1
+    A, B = _operands(dtype, M, N, K, seed=M + 3 * K)
+    dA, dB = to_device(A), to_device(B)
+    rotated = gemm(lib, dtype, "pipelined", dA, dB)
+    prev = lib.tdg_set_debug_flags(lib.TDG_DEBUG_NO_K_ROTATION)
+    try:
+        plain = gemm(lib, dtype, "pipelined", dA, dB)
+    finally:
+        lib.tdg_set_debug_flags(prev)
+    _check(dtype, rotated, A, B)
+    _check(dtype, plain, A, B)
+    if dtype == I8:
+        assert torch.equal(rotated, plain)
+        assert torch.equal(rotated, gemm(lib, dtype, "single", dA, dB))
+
+
 def test_invalid_arguments_are_rejected(lib):
     import torch
     A = torch.zeros((64, 64), dtype=torch.int8, device="cuda")

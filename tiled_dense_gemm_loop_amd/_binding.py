@@ -28,6 +28,7 @@ TDG_VARIANT_SINGLE = 1
 TDG_VARIANT_REG_PREFETCH = 2
 TDG_VARIANT_DIRECT_LDS = 3
 TDG_DEBUG_POISON_LDS = 1
+TDG_DEBUG_NO_K_ROTATION = 2
 
 VARIANT_NAMES = {0: "auto", 1: "single", 2: "reg_prefetch", 3: "direct_lds"}
 
@@ -63,7 +64,7 @@ class TdgPlanInfo(ctypes.Structure):
                 ("wg_per_cu", ctypes.c_int), ("num_tiles", ctypes.c_int64),
                 ("grid", ctypes.c_int64), ("est_regs", ctypes.c_int), ("guarded", ctypes.c_int),
                 ("need_bytes_per_clk", ctypes.c_double), ("mfma_per_load", ctypes.c_double),
-                ("pipelined", ctypes.c_int)]
+                ("pipelined", ctypes.c_int), ("k_rotated", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

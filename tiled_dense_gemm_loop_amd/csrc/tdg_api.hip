@@ -167,6 +167,13 @@ int est_regs(int bm, int bn, int bkb, int waves, int variant) {
     return acc + staging + frags + 24;
 }
 
+// Whether tile rows walk K from their own offsets: when all of B fits in half
+// an XCD's 4 MB L2, B is served from L2 in any order, and rotating the walk
+// spreads A's concurrent HBM reads over the channels.
+bool k_rotation(int dtype, int64_t N, int64_t K) {
+    return (double)K * (double)N * elem_size(dtype) <= (double)(2 << 20);
+}
+
 // The pages' planning arithmetic for one tile and problem.
 void tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant, int64_t M,
                   int64_t N, int64_t K, tdg_plan_info *info) {
@@ -201,6 +208,7 @@ void tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int 
     const double loads = bytes / 1024.0;  // 64 lanes x 16 bytes per wave instruction
     info->mfma_per_load = mfmas / loads;
     info->pipelined = variant != TDG_VARIANT_SINGLE && info->num_tiles >= 2;
+    info->k_rotated = k_rotation(dtype, N, K) ? 1 : 0;
 }
 
 void fill_info(const KernelEntry &e, int variant, int stages, int64_t M, int64_t N, int64_t K,
@@ -469,6 +477,7 @@ int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, 
     args.tiles_n = (int)ceil_div(N, e.bn);
     args.k_tiles = (int)ceil_div(K, cfg_bk(e));
     args.flags = tdg::debug_flags.load(std::memory_order_relaxed);
+    args.k_rotate = k_rotation(dtype, N, K) && !(args.flags & TDG_DEBUG_NO_K_ROTATION) ? 1 : 0;
     const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
     if (grid > INT32_MAX) return TDG_ERR_UNSUPPORTED;
 
@@ -593,7 +602,7 @@ int tdg_config_at(int dtype, int index, tdg_config *out) {
 }
 
 int tdg_set_debug_flags(int flags) {
-    if (flags & ~TDG_DEBUG_POISON_LDS) return TDG_ERR_INVALID_ARG;
+    if (flags & ~(TDG_DEBUG_POISON_LDS | TDG_DEBUG_NO_K_ROTATION)) return TDG_ERR_INVALID_ARG;
     return tdg::debug_flags.exchange(flags);
 }
 

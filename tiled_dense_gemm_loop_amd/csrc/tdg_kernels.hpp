@@ -73,6 +73,7 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int k_tiles;  // ceil(K / BK); 0 when K == 0 (C is then zero-filled)
     int flags;    // TDG_DEBUG_* bits
+    int k_rotate; // 1: tile row tm walks its K tiles from tm mod k_tiles
 };
 
 // Compile-time geometry of one configuration.
@@ -417,6 +418,17 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     u32x4 ra[G::CA], rb[G::CB];  // register staging (SINGLE / REG)
     uint32_t fix_a[G::CA], fix_b[G::CB];  // their corrections (GUARD)
 
+    // K-tile rotation (k_rotate, chosen on the host when all of B fits in
+    // half an XCD's L2): tile row tm starts its K walk at tile tm mod nt and
+    // wraps.  Workgroups of one tile row share A panels and stay in lock
+    // step; B is read from L2 in any order.  What changes is A's pattern in
+    // HBM: without the rotation every workgroup reads the same K columns of
+    // its rows at once, and with a row stride that is a multiple of the HBM
+    // channel interleave those reads land on a few channels.  `kt` below is
+    // the position in the walk; phys() is the K tile it loads.  Every loop
+    // form uses the same walk, so their results stay bitwise identical.
+    const int krot = args.k_rotate && nt > 0 ? tm % nt : 0;
+    auto phys = [&](int kt) { return kt + krot >= nt ? kt + krot - nt : kt + krot; };
     auto a_ptr = [&](int kt, int i) {
         return a_base + (int64_t)kt * G::BKB + (int64_t)(i * A_RSTEP) * lda_b;
     };
@@ -424,6 +436,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
         return b_base + (int64_t)(kt * G::BK + i * B_RSTEP) * ldb_b;
     };
     auto load_regs = [&](int kt) {
+        kt = phys(kt);
         if (!GUARD) {
 #pragma unroll
             for (int i = 0; i < G::CA; i++) ra[i] = *(const u32x4 *)(a_ptr(kt, i) + a_voff);
@@ -502,6 +515,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     const bool b_col_ok = n0 + b_c * EPC < args.N;
     const int a_kc = a_c * EPC;  // first k of this thread's A chunk within a tile
     auto issue_direct_one = [&](uint32_t st_off, int kt, int d) {
+        kt = phys(kt);
         const uint32_t wbase = smem_addr + st_off + (uint32_t)wave * 1024u;
         if constexpr (GUARD) {
             const unsigned char *src;
