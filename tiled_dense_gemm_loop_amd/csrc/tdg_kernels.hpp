@@ -743,7 +743,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // lane l of block (mi, ni) holds rows 8*(v/4) + 4*(l/32) + v%4, column l%32.
     // Every tile load has landed by now; saying so with a counted wait keeps
     // the compiler from guarding the stores' address registers (once tile
-    // load destinations) with waits on the stores themselves.
+    // load destinations) with waits on the stores themselves.  The stores are
+    // non-temporal: C is written once and not read back by this kernel, and
+    // streaming it past the L2 keeps the A and B lines that workgroups still
+    // running read (FP16 / INT8 4096^3: about 1% faster).
     wait_vmcnt<0>();
     out_t *C = (out_t *)args.C;
     const int col_l = lane & 31, rq = (lane >> 5) * 4;
@@ -756,7 +759,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             for (int v = 0; v < 16; v++) {
                 const int row = m0 + wm * G::WTM + mi * 32 + (v >> 2) * 8 + rq + (v & 3);
                 if (!GUARD || (row < args.M && col < args.N))
-                    C[(int64_t)row * args.ldc + col] = acc[mi][ni][v];
+                    __builtin_nontemporal_store(acc[mi][ni][v], &C[(int64_t)row * args.ldc + col]);
             }
         }
 }
