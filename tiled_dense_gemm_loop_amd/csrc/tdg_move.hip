@@ -22,7 +22,8 @@
 // The copy marks its global accesses non-temporal: nothing is read twice, and
 // on a 1 GiB copy that measured 4-7% more bandwidth.  (The same hint made
 // VEC slower, at both sizes measured, so VEC keeps ordinary accesses.)
-// Tiles are 64 x 64 elements, one workgroup of 256 threads (4 waves) each.
+// Tiles are 64 x 64 elements, one workgroup of 256 threads (4 waves) each;
+// the transposes take them in diagonal order (tile_origin).
 // Partial tiles at the matrix edges take element-wise, bounds-checked paths;
 // VEC runs its vector path on whole tiles of 16-byte aligned operands and
 // falls back to the swizzled element-wise path elsewhere.
@@ -50,13 +51,25 @@ struct MoveArgs {
     int64_t ldi, ldo;
     int rows, cols;
     int tiles_c;  // tiles along a row of the input
+    int tiles_r;  // tiles along a column of the input
     int vec_ok;   // 16-byte aligned bases and leading dimensions
+    int diagonal; // 1: diagonal tile order (the transposes)
 };
 
+// Workgroup -> tile.  The copy walks the tiles row by row.  A transpose walks
+// them diagonally: workgroup t takes tile column t mod tiles_c and tile row
+// (t / tiles_c + t mod tiles_c) mod tiles_r, a bijection.  Row by row,
+// workgroups running side by side would write output tiles that differ only
+// in their output rows; with a power-of-two row length those addresses are a
+// multiple of the HBM channel interleave apart and crowd a few channels.
+// Diagonally, neighbours write at neighbouring output column offsets and read
+// at neighbouring input column offsets, so both spread over the channels.
 __device__ __forceinline__ void tile_origin(const MoveArgs &a, int &r0, int &c0) {
     const int t = blockIdx.x;
-    r0 = (t / a.tiles_c) * TILE;
-    c0 = (t % a.tiles_c) * TILE;
+    const int q = t / a.tiles_c, tx = t % a.tiles_c;
+    const int ty = a.diagonal ? (int)(((int64_t)q + tx) % a.tiles_r) : q;
+    r0 = ty * TILE;
+    c0 = tx * TILE;
 }
 
 __device__ __forceinline__ bool whole_tile(const MoveArgs &a, int r0, int c0) {
@@ -259,7 +272,9 @@ int launch_move(int method, bool transpose, int64_t rows, int64_t cols, const fl
     a.rows = (int)rows;
     a.cols = (int)cols;
     a.tiles_c = (int)((cols + TILE - 1) / TILE);
-    const int64_t tiles = ((rows + TILE - 1) / TILE) * (int64_t)a.tiles_c;
+    a.tiles_r = (int)((rows + TILE - 1) / TILE);
+    a.diagonal = transpose ? 1 : 0;
+    const int64_t tiles = (int64_t)a.tiles_r * a.tiles_c;
     if (tiles > INT32_MAX) return TDG_ERR_UNSUPPORTED;
     a.vec_ok = ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0) && ldi % 4 == 0 && ldo % 4 == 0;
 
