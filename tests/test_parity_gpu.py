@@ -336,6 +336,39 @@ def test_tails_at_every_page_offset(lib, dtype):
         _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
 
 
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_random_shapes_strides_and_configs(lib, dtype):
+    """A seeded sweep over the space the other tests sample by hand: random
+    M, N, K (1..700), leading dimensions padded by 0..20 elements, base
+    offsets of 0..3 elements for A, B and C, and for each case the planner's
+    choice plus a random built configuration (tile, waves, loop form,
+    stages).  Every result against the oracle; C's padding untouched."""
+    import random
+    import torch
+    rng = random.Random({F16: 11, I8: 12, F32: 13}[dtype])
+    code = CODE[dtype]
+    configs = [lib.tdg_config_at(code, i) for i in range(lib.tdg_config_count(code))]
+    out_t = torch.int32 if dtype == I8 else torch.float32
+    for case in range(24):
+        M, N, K = rng.randint(1, 700), rng.randint(1, 700), rng.randint(1, 700)
+        pa, pb, pc = rng.randint(0, 20), rng.randint(0, 20), rng.randint(0, 20)
+        oa, ob, oc = rng.randint(0, 3), rng.randint(0, 3), rng.randint(0, 3)
+        bigA, bigB = _operands(dtype, M, N + pb + ob, K + pa + oa, seed=1000 + case)
+        bigB = bigB[:K, :]                   # K rows, ldb = N + pb + ob
+        A, B = bigA[:, oa:oa + K], bigB[:, ob:ob + N]
+        dBigA, dBigB = to_device(bigA), to_device(bigB)
+        dA, dB = dBigA[:, oa:oa + K], dBigB[:, ob:ob + N]
+        for cfg in (None, rng.choice(configs)):
+            bigC = torch.full((M, N + pc + oc), -7, dtype=out_t, device="cuda")
+            C = bigC[:, oc:oc + N]
+            if cfg is None:
+                gemm(lib, dtype, "pipelined", dA, dB, C)
+            else:
+                gemm(lib, dtype, "ex", dA, dB, C, cfg=cfg)
+            _check(dtype, C, A, B)
+            assert torch.all(bigC[:, :oc] == -7) and torch.all(bigC[:, oc + N:] == -7), (case, cfg)
+
+
 def test_output_leading_dimension(lib):
     import torch
     M, N, K = 256, 256, 192
