@@ -404,6 +404,32 @@ def main():
     else:
         achieved, peak, r_unit = round(gbs, 1), HBM_PEAK_GBS, "GB/s"
         measured = ceilings.get("copy_gbs")
+    # The metric has three parts: FP16 and INT8 4096^3 against the dense MFMA
+    # peak, and the skinny product against HBM.  `value` is the first; the
+    # three together, each with its fraction of the data-sheet peak and of
+    # the measured ceiling, go in `metric_parts` (from the pipelined rows).
+    # Each part is timed like the headline (args.steps launches after
+    # args.warmup), past the power controller's first milliseconds.
+    parts = None
+    if not args.no_table:
+        def part(name, use_gbs, peak_v, unit_v, ceiling_key):
+            w = si.WORKLOADS[name]
+            if name == wl.name:
+                t = ms
+            else:
+                _, _, da, db, c = device_operands(w)
+                t = time_launches(launcher(tdg, w, da, db, c, "pipelined"), args.steps, args.warmup)
+                del da, db, c
+                torch.cuda.empty_cache()
+            tp, bw = throughput(w, t)
+            v = round(bw if use_gbs else tp, 1)
+            c = ceilings.get(ceiling_key)
+            return {"value": v, "unit": unit_v, "us": round(t * 1e3, 2), "peak": peak_v,
+                    "frac_of_peak": round(v / peak_v, 4),
+                    "frac_of_measured": round(v / c, 4) if c else None}
+        parts = {"fp16_4096": part("fp16_4096", False, PEAK["f16"], "TFLOP/s", "mfma_f16_tflops"),
+                 "int8_4096": part("int8_4096", False, PEAK["i8"], "TOP/s", "mfma_i8_tops"),
+                 "fp16_skinny": part("fp16_skinny", True, HBM_PEAK_GBS, "GB/s", "copy_gbs")}
     # the headline is the roofline's own quantity: operations per second for
     # an MFMA-bound product, bytes per second for an HBM-bound one
     line = {
@@ -427,6 +453,7 @@ def main():
                      "unit": r_unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "measured_peak": measured,
                      "frac_of_measured": round(achieved / measured, 4) if measured else None},
+        "metric_parts": parts,
         "measured_ceilings": ceilings,
         "launches": launches,
         "cold": cold,
