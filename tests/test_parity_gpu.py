@@ -369,6 +369,48 @@ def test_random_shapes_strides_and_configs(lib, dtype):
             assert torch.all(bigC[:, :oc] == -7) and torch.all(bigC[:, oc + N:] == -7), (case, cfg)
 
 
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 100000), (1, 3000, 5000), (3000, 1, 5000), (2, 2, 65536)])
+def test_extreme_aspect_ratios(lib, dtype, M, N, K):
+    """A dot product, a single row, a single column and a 2 x 2 output over a
+    long K: one workgroup or one tile row/column, long K walks."""
+    A, B = _operands(dtype, M, N, K, seed=M + 2 * N + 3 * K)
+    dA, dB = to_device(A), to_device(B)
+    for kind in ("single", "pipelined"):
+        _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_largest_leading_dimensions(lib, dtype):
+    """The largest 16-byte aligned leading dimensions the per-lane 32-bit
+    offsets accept (64 * ld * sizeof(T) + 256 < 2^31) on the unguarded
+    direct-to-LDS path: whole 128 x 128 x 128 tiles inside matrices whose
+    rows are 32 MiB apart (A and B ~4.3 GB each, C ~8.6 GB)."""
+    import torch
+    es = 2 if dtype == F16 else 1
+    ld = ((1 << 31) - 257) // (64 * es)
+    ld -= ld % (16 // es)                     # keep rows 16-byte aligned
+    assert 64 * ld * es + 256 < (1 << 31)
+    M = N = K = 128
+    A, B = _operands(dtype, M, N, K, seed=77)
+    tdt = torch.float16 if dtype == F16 else torch.int8
+    bigA = torch.empty((M, ld), dtype=tdt, device="cuda")
+    bigB = torch.empty((K, ld), dtype=tdt, device="cuda")
+    bigC = torch.empty((M, ld), dtype=torch.float32 if dtype == F16 else torch.int32, device="cuda")
+    try:
+        bigA[:, :K] = to_device(A)
+        bigB[:, :N] = to_device(B)
+        C = bigC[:, :N]
+        cfg, info = lib.tdg_plan(CODE[dtype], M, N, K)
+        assert info["guarded"] == 0
+        for kind in ("single", "pipelined"):
+            gemm(lib, dtype, kind, bigA[:, :K], bigB[:, :N], C)
+            _check(dtype, C, A, B)
+    finally:
+        del bigA, bigB, bigC
+        torch.cuda.empty_cache()
+
+
 def test_output_leading_dimension(lib):
     import torch
     M, N, K = 256, 256, 192
