@@ -210,21 +210,9 @@ __device__ static __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// Wait until at most r * IPT vector-memory operations are outstanding, for a
-// runtime r in [0, R]: each case is its own immediate.
-template <int R, int IPT>
-__device__ static __forceinline__ void wait_vmcnt_upto(int r) {
-    if constexpr (R <= 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (r >= R) wait_vmcnt<R * IPT>();
-        else wait_vmcnt_upto<R - 1, IPT>(r);
-    }
-}
-
-// Sixteen zero bytes: the DMA source of every chunk that lies outside A or B
-// on the bounds-checked direct-to-LDS path, so that chunk lands in LDS as
-// zeros while every lane still issues the same DMA instruction.
+// Sixteen zero bytes: the source of every chunk that lies outside A or B on
+// the bounds-checked paths, so that chunk lands in LDS as zeros while every
+// lane still issues the same load or DMA instruction.
 static __device__ __attribute__((aligned(16))) const uint32_t tdg_zero16[4] = {0u, 0u, 0u, 0u};
 
 // Workgroup -> C tile.  Workgroups are dealt round-robin to the 8 XCDs, so
@@ -552,13 +540,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     };
 
     // MFMA tile micro-kernel over one LDS buffer.  The fragments of K step
-    // s+1 are requested from LDS before the MFMAs of step s are issued (two
-    // register sets, fa/fb[s & 1]), so the LDS latency hides behind a whole
-    // step of matrix work; the scheduling barriers keep the compiler from
-    // sinking the reads back next to their first use.  At the last step the
-    // loop-specific `boundary` runs before the last MFMAs: it publishes the
-    // next tile and reads that tile's first fragments into set 0, so the
-    // tile change costs no exposed LDS latency either.
+    // s + FD are requested from LDS while the MFMAs of step s issue (FD
+    // register sets ahead), so the LDS latency hides behind matrix work; the
+    // scheduling barriers keep the compiler from sinking the reads back next
+    // to their first use.  When the reads run past the tile, the
+    // loop-specific `boundary` runs first: it publishes the next tile, whose
+    // first fragments are then read into their sets, so the tile change
+    // costs no exposed LDS latency either.
     static_assert(G::KSTEPS % 2 == 0, "fragment set parity must repeat per tile");
 #ifndef TDG_FRAG_DIST
 #define TDG_FRAG_DIST 2
