@@ -325,3 +325,40 @@ def test_k_rotation_rule():
     for args, want in cases:
         _, info = tdg.tdg_plan(*args)
         assert info["k_rotated"] == want, args
+
+
+def _plan_str(code, M, N, K, **req):
+    cfg, _ = tdg.tdg_plan(code, M, N, K, cfg=req or None)
+    return "%dx%d w%d s%d %s" % (cfg["bm"], cfg["bn"], cfg["waves"], cfg["lds_stages"],
+                                 tdg.VARIANT_NAMES[cfg["variant"]])
+
+
+def test_planner_picks_by_predicted_time():
+    """The planner minimises the measured-time model over the built direct-
+    to-LDS configurations.  Where the older rule (the largest tile that still
+    fills all 256 CUs) lost 26-51% on MI355X, it now takes the larger tile
+    with fewer workgroups; the benchmark shapes keep their configurations."""
+    F16, I8 = tdg.TDG_DTYPE_F16F32, tdg.TDG_DTYPE_I8I32
+    assert _plan_str(F16, 4096, 4096, 4096) == "256x256 w8 s2 direct_lds"
+    assert _plan_str(I8, 4096, 4096, 4096) == "256x256 w8 s2 direct_lds"
+    assert _plan_str(F16, 1024, 1024, 1024) == "64x64 w4 s4 direct_lds"
+    assert _plan_str(F16, 16384, 64, 8192) == "64x64 w4 s4 direct_lds"
+    assert _plan_str(F16, 4000, 4000, 4000) == "256x256 w8 s2 direct_lds"
+    # 144 and 196 workgroups of 256 x 256 beat 288 and 392 of 256 x 128
+    assert _plan_str(F16, 3072, 3072, 3072) == "256x256 w8 s2 direct_lds"
+    assert _plan_str(F16, 3584, 3584, 3584) == "256x256 w8 s2 direct_lds"
+    # 144 workgroups of 128 x 128 beat 288 of 128 x 64
+    assert _plan_str(F16, 1536, 1536, 1536) == "128x128 w4 s4 direct_lds"
+    assert _plan_str(I8, 2560, 2560, 2560) == "128x128 w4 s2 direct_lds"
+
+
+def test_planner_respects_partial_requests():
+    """A request that fixes part of the configuration is completed within it;
+    one outside the measured table (a 64-byte K tile) falls back to the tile
+    rule and still resolves."""
+    F16 = tdg.TDG_DTYPE_F16F32
+    assert _plan_str(F16, 4096, 4096, 4096, waves=4).startswith("256x256 w4")
+    assert _plan_str(F16, 4096, 4096, 4096, bm=128, bn=128).startswith("128x128 w4")
+    assert _plan_str(F16, 2048, 2048, 2048, bm=128, bn=128, lds_stages=2) == "128x128 w4 s2 direct_lds"
+    cfg, _ = tdg.tdg_plan(F16, 4096, 4096, 4096, cfg={"bk": 32})
+    assert cfg["bk"] == 32 and cfg["bm"] == 256

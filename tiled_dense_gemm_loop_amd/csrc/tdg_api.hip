@@ -218,63 +218,192 @@ void fill_info(const KernelEntry &e, int variant, int stages, int64_t M, int64_t
     info->guarded = guarded ? 1 : 0;
 }
 
-// Wave count and ring depth per tile shape that measured fastest for the
-// direct-to-LDS loop on MI355X (4096^3 FP16 and INT8, 2048^3 FP16,
-// 16384 x 64 x 8192 FP16);
-// tiles not listed use 4 waves and a two-buffer ring.
-struct Measured {
-    int bm, bn, bkb, waves, stages;
+// Measured kernel time of every built direct-to-LDS configuration with a
+// 128-byte K tile, as a function of the number of workgroups n and of K:
+// T(n, K) = a + b * K microseconds, interpolated between the n of kPerfN.
+// Measured on one MI355X at K = 1024 and K = 4096 with the tiles laid out
+// close to square, FP16 and INT8 as HIP-graph replays, FP32 as back-to-back
+// launches; each series is non-decreasing in n (tune_planner.py in the
+// package measures and prints this table).  The rows of a dtype are in
+// preference order for near ties.
+struct PerfRow {
+    int dtype, bm, bn, waves, stages;
+    float a[12], b[12];
 };
-const Measured kMeasured[] = {
-    {256, 256, 128, 8, 2},
-    {128, 128, 128, 4, 4},  // FP16 2048^3: 24.6 us with 4 buffers, 26.4 with 2
-    {128, 64, 128, 4, 4},
-    {64, 64, 128, 4, 4},
+const int kPerfN[12] = {32, 64, 128, 192, 256, 320, 384, 512, 768, 1024, 1536, 2304};
+const PerfRow kPerf[] = {
+    {0, 256, 256, 8, 2, {6.77f, 6.29f, 6.54f, 9.68f, 13.94f, 18.70f, 18.39f, 23.92f, 33.90f, 41.53f, 57.69f, 84.83f},
+     {0.015843f, 0.016309f, 0.018265f, 0.021527f, 0.024521f, 0.039971f, 0.042311f, 0.048005f, 0.071582f, 0.095768f, 0.144336f, 0.216790f}},
+    {0, 256, 256, 4, 2, {6.22f, 8.06f, 10.61f, 12.78f, 16.02f, 20.70f, 21.60f, 26.80f, 36.89f, 45.68f, 62.36f, 92.92f},
+     {0.018724f, 0.018278f, 0.019157f, 0.022106f, 0.025075f, 0.042393f, 0.043271f, 0.048988f, 0.073167f, 0.097637f, 0.148610f, 0.221341f}},
+    {0, 256, 128, 4, 2, {3.17f, 3.17f, 4.05f, 6.29f, 7.77f, 9.70f, 9.71f, 12.76f, 19.56f, 23.27f, 33.60f, 53.08f},
+     {0.012070f, 0.012070f, 0.012207f, 0.012708f, 0.014417f, 0.025837f, 0.026351f, 0.028906f, 0.042588f, 0.058900f, 0.087894f, 0.130293f}},
+    {0, 256, 128, 4, 3, {4.70f, 4.35f, 4.51f, 5.89f, 7.79f, 11.67f, 10.76f, 13.71f, 18.86f, 22.03f, 35.12f, 56.21f},
+     {0.011686f, 0.012028f, 0.012594f, 0.013633f, 0.015039f, 0.025820f, 0.026803f, 0.029248f, 0.044447f, 0.061670f, 0.090225f, 0.133105f}},
+    {0, 128, 128, 4, 4, {4.13f, 3.83f, 3.70f, 4.40f, 4.79f, 7.24f, 7.12f, 6.92f, 10.00f, 12.14f, 18.23f, 29.88f},
+     {0.006149f, 0.006442f, 0.006849f, 0.007142f, 0.008298f, 0.014173f, 0.014284f, 0.016413f, 0.024785f, 0.033926f, 0.051003f, 0.074248f}},
+    {0, 128, 128, 4, 2, {-0.17f, -0.17f, -0.43f, 2.96f, 3.32f, 4.75f, 4.00f, 5.62f, 8.58f, 10.81f, 14.00f, 22.82f},
+     {0.010033f, 0.010033f, 0.010280f, 0.009811f, 0.010462f, 0.011647f, 0.013223f, 0.015072f, 0.023958f, 0.029417f, 0.044141f, 0.066022f}},
+    {0, 128, 128, 4, 3, {3.94f, 3.94f, 3.80f, 4.28f, 5.18f, 7.51f, 6.97f, 6.27f, 9.67f, 13.23f, 20.39f, 25.15f},
+     {0.007936f, 0.007936f, 0.008203f, 0.008643f, 0.009186f, 0.016755f, 0.017285f, 0.019479f, 0.029170f, 0.038005f, 0.055957f, 0.087878f}},
+    {0, 128, 64, 4, 4, {3.08f, 3.08f, 2.88f, 3.07f, 3.22f, 5.03f, 5.03f, 5.48f, 5.10f, 9.90f, 13.58f, 17.33f},
+     {0.005107f, 0.005107f, 0.005371f, 0.005492f, 0.005726f, 0.010423f, 0.010423f, 0.010911f, 0.017835f, 0.022386f, 0.033701f, 0.050964f}},
+    {0, 128, 64, 4, 2, {-0.86f, -1.04f, -1.27f, -0.19f, -0.53f, 1.85f, 2.14f, 4.13f, 4.03f, 6.81f, 6.98f, 8.02f},
+     {0.008848f, 0.009027f, 0.009339f, 0.009245f, 0.009583f, 0.009395f, 0.009323f, 0.009808f, 0.015495f, 0.021530f, 0.029329f, 0.044303f}},
+    {0, 128, 64, 4, 6, {3.70f, 3.70f, 3.76f, 3.97f, 4.00f, 6.69f, 6.69f, 6.81f, 8.60f, 12.69f, 17.86f, 23.08f},
+     {0.006006f, 0.006006f, 0.006110f, 0.006348f, 0.006689f, 0.012233f, 0.012233f, 0.013005f, 0.019616f, 0.025550f, 0.037985f, 0.057363f}},
+    {0, 64, 64, 4, 4, {2.89f, 2.89f, 2.89f, 3.03f, 3.15f, 1.25f, 1.36f, 1.40f, 4.49f, 4.46f, 6.03f, 7.97f},
+     {0.003490f, 0.003490f, 0.003555f, 0.003581f, 0.003682f, 0.007002f, 0.006976f, 0.007884f, 0.010915f, 0.013770f, 0.019769f, 0.028906f}},
+    {0, 64, 64, 4, 2, {-1.20f, -1.20f, -1.29f, -1.17f, -1.31f, 0.31f, 0.41f, 2.20f, 3.17f, 4.01f, 5.04f, 6.68f},
+     {0.007660f, 0.007660f, 0.007790f, 0.007965f, 0.008252f, 0.007946f, 0.007923f, 0.007855f, 0.010518f, 0.013734f, 0.018910f, 0.028861f}},
+    {0, 64, 64, 4, 8, {3.45f, 3.45f, 3.46f, 3.50f, 3.52f, 5.31f, 5.43f, 5.57f, 7.18f, 9.51f, 12.85f, 17.71f},
+     {0.003353f, 0.003353f, 0.003408f, 0.003548f, 0.003623f, 0.006868f, 0.006839f, 0.007028f, 0.011003f, 0.014186f, 0.021520f, 0.032646f}},
+    {1, 256, 256, 8, 2, {6.69f, 6.69f, 7.87f, 10.51f, 13.65f, 18.41f, 18.68f, 24.17f, 34.51f, 41.58f, 59.17f, 84.37f},
+     {0.007848f, 0.007848f, 0.008480f, 0.010150f, 0.012184f, 0.019854f, 0.020993f, 0.023818f, 0.035036f, 0.047500f, 0.071198f, 0.108330f}},
+    {1, 256, 256, 4, 2, {6.71f, 7.25f, 9.36f, 12.47f, 15.77f, 20.82f, 21.89f, 26.63f, 36.92f, 45.14f, 63.53f, 93.19f},
+     {0.009320f, 0.009294f, 0.009756f, 0.010752f, 0.012409f, 0.020918f, 0.021250f, 0.024095f, 0.035811f, 0.047829f, 0.072070f, 0.110345f}},
+    {1, 256, 128, 4, 2, {3.81f, 3.81f, 4.55f, 6.14f, 7.98f, 10.22f, 9.84f, 12.17f, 17.77f, 21.86f, 30.96f, 48.23f},
+     {0.006250f, 0.006250f, 0.006139f, 0.006410f, 0.007308f, 0.013161f, 0.013538f, 0.014642f, 0.021921f, 0.029548f, 0.044447f, 0.067640f}},
+    {1, 256, 128, 4, 3, {4.98f, 4.98f, 5.69f, 7.01f, 8.34f, 11.78f, 11.65f, 14.02f, 19.37f, 24.69f, 34.99f, 49.28f},
+     {0.005794f, 0.005794f, 0.005788f, 0.006344f, 0.007321f, 0.012816f, 0.013079f, 0.014323f, 0.021758f, 0.029580f, 0.045208f, 0.068698f}},
+    {1, 128, 128, 4, 4, {4.24f, 4.24f, 4.29f, 4.79f, 5.41f, 8.12f, 8.48f, 8.56f, 12.01f, 14.95f, 20.73f, 31.20f},
+     {0.003236f, 0.003236f, 0.003340f, 0.003584f, 0.004176f, 0.007279f, 0.007191f, 0.007887f, 0.012035f, 0.016507f, 0.025661f, 0.038483f}},
+    {1, 128, 128, 4, 2, {2.92f, 2.92f, 2.24f, 2.98f, 3.91f, 4.50f, 4.50f, 5.94f, 8.51f, 11.44f, 16.29f, 21.57f},
+     {0.004336f, 0.004336f, 0.005000f, 0.005098f, 0.005286f, 0.006807f, 0.006807f, 0.007454f, 0.012572f, 0.014378f, 0.021429f, 0.033288f}},
+    {1, 128, 128, 4, 3, {4.00f, 4.00f, 4.02f, 4.68f, 5.59f, 7.65f, 7.92f, 8.37f, 11.99f, 14.12f, 19.94f, 29.37f},
+     {0.003968f, 0.003968f, 0.004063f, 0.004121f, 0.004411f, 0.008350f, 0.008285f, 0.008763f, 0.014046f, 0.018988f, 0.028105f, 0.041693f}},
+    {1, 128, 64, 4, 4, {3.37f, 3.37f, 3.45f, 3.25f, 3.56f, 5.26f, 4.80f, 5.83f, 7.17f, 9.57f, 15.75f, 19.49f},
+     {0.002572f, 0.002572f, 0.002552f, 0.003018f, 0.002985f, 0.005339f, 0.005827f, 0.005664f, 0.008796f, 0.011924f, 0.017139f, 0.026686f}},
+    {1, 128, 64, 4, 2, {2.34f, 2.34f, 2.26f, 1.99f, 1.72f, 2.99f, 2.56f, 4.12f, 3.92f, 5.61f, 8.09f, 7.92f},
+     {0.003958f, 0.003958f, 0.004040f, 0.004704f, 0.005068f, 0.005000f, 0.005723f, 0.005882f, 0.008750f, 0.012041f, 0.016445f, 0.025176f}},
+    {1, 128, 64, 4, 6, {3.67f, 3.67f, 3.84f, 4.02f, 4.29f, 6.15f, 6.28f, 7.60f, 9.56f, 12.37f, 20.80f, 26.84f},
+     {0.003210f, 0.003210f, 0.003193f, 0.003314f, 0.003447f, 0.006582f, 0.006549f, 0.006413f, 0.009932f, 0.013389f, 0.018991f, 0.029076f}},
+    {1, 64, 64, 4, 4, {2.92f, 2.92f, 2.92f, 2.59f, 2.71f, 2.82f, 2.87f, 3.00f, 3.61f, 4.10f, 7.34f, 8.01f},
+     {0.001790f, 0.001790f, 0.001790f, 0.002246f, 0.002233f, 0.003568f, 0.003880f, 0.004307f, 0.006429f, 0.008646f, 0.011940f, 0.017878f}},
+    {1, 64, 64, 4, 2, {2.86f, 2.84f, 2.77f, 1.34f, 1.58f, 2.14f, 1.80f, 2.41f, 1.87f, 3.60f, 4.81f, 5.07f},
+     {0.001979f, 0.001999f, 0.002204f, 0.003851f, 0.003851f, 0.003997f, 0.004518f, 0.004600f, 0.006855f, 0.008327f, 0.011286f, 0.017695f}},
+    {1, 64, 64, 4, 8, {3.36f, 3.36f, 3.34f, 3.56f, 3.55f, 5.10f, 4.70f, 5.28f, 7.12f, 9.50f, 14.80f, 21.06f},
+     {0.001868f, 0.001868f, 0.001914f, 0.002194f, 0.002204f, 0.003835f, 0.004574f, 0.004469f, 0.006768f, 0.008763f, 0.012832f, 0.018688f}},
+    {2, 256, 256, 8, 2, {10.57f, 9.31f, 11.91f, 20.51f, 30.15f, 20.15f, 19.50f, 30.60f, 28.52f, 37.24f, 58.85f, 81.72f},
+     {0.218822f, 0.220052f, 0.220804f, 0.218704f, 0.217191f, 0.435628f, 0.436260f, 0.438535f, 0.662718f, 0.882604f, 1.319268f, 1.980283f}},
+    {2, 128, 128, 4, 2, {5.57f, 5.78f, 5.47f, 3.07f, 3.36f, 7.70f, 7.70f, 4.88f, -0.56f, 12.36f, 18.32f, -53.73f},
+     {0.057122f, 0.057070f, 0.057803f, 0.061064f, 0.063021f, 0.111924f, 0.111924f, 0.116875f, 0.183105f, 0.225020f, 0.338024f, 0.580762f}},
+    {2, 128, 128, 4, 3, {5.35f, 5.55f, 4.86f, 2.67f, 3.59f, 9.95f, 9.95f, 7.59f, 11.57f, 12.28f, 20.84f, 23.93f},
+     {0.057891f, 0.057842f, 0.058584f, 0.061829f, 0.062998f, 0.117360f, 0.117360f, 0.121416f, 0.179684f, 0.239844f, 0.357780f, 0.537057f}},
+    {2, 128, 64, 4, 4, {5.65f, 5.65f, 5.53f, 4.60f, 4.05f, 7.46f, 7.46f, 6.98f, 9.94f, 13.54f, 13.88f, 20.59f},
+     {0.030182f, 0.030182f, 0.030306f, 0.031214f, 0.032650f, 0.061992f, 0.061992f, 0.063454f, 0.094049f, 0.123522f, 0.187900f, 0.281540f}},
+    {2, 128, 64, 4, 2, {4.95f, 4.95f, 4.93f, 4.50f, 3.95f, 6.19f, 6.50f, 7.73f, 3.93f, 26.93f, 11.16f, 19.12f},
+     {0.030426f, 0.030426f, 0.030560f, 0.031615f, 0.033219f, 0.058350f, 0.058275f, 0.058675f, 0.090186f, 0.120094f, 0.172370f, 0.254694f}},
+    {2, 64, 64, 4, 4, {3.67f, 3.67f, 3.62f, 4.13f, 4.45f, 3.83f, 3.78f, 4.43f, 6.00f, 5.38f, 1.14f, 10.07f},
+     {0.016243f, 0.016243f, 0.016289f, 0.016517f, 0.016693f, 0.030179f, 0.030225f, 0.030381f, 0.059847f, 0.060563f, 0.095456f, 0.151530f}},
+    {2, 64, 64, 4, 2, {3.91f, 3.91f, 3.73f, 3.63f, 4.46f, 4.69f, 4.97f, 4.68f, 4.27f, 2.28f, 5.06f, 8.20f},
+     {0.016169f, 0.016169f, 0.016351f, 0.016449f, 0.016914f, 0.029860f, 0.029792f, 0.030332f, 0.045706f, 0.062083f, 0.103734f, 0.145026f}},
 };
 
-const Measured *measured_for(int bm, int bn, int bkb) {
-    for (const Measured &m : kMeasured)
-        if (m.bm == bm && m.bn == bn && m.bkb == bkb) return &m;
+// Interpolated T(x, K) of one row; below the first n the time is flat, and
+// K below 1024 is taken as 1024 (small products sit at the launch floor,
+// where the line through the two measured K says nothing).
+double perf_at(const PerfRow &r, int64_t x, int64_t K) {
+    const double k = (double)(K < 1024 ? 1024 : K);
+    constexpr int P = (int)(sizeof(kPerfN) / sizeof(kPerfN[0]));
+    if (x <= kPerfN[0]) return r.a[0] + r.b[0] * k;
+    for (int i = 1; i < P; i++) {
+        if (x <= kPerfN[i]) {
+            const double f = (double)(x - kPerfN[i - 1]) / (double)(kPerfN[i] - kPerfN[i - 1]);
+            const double a = r.a[i - 1] + f * (r.a[i] - r.a[i - 1]);
+            const double b = r.b[i - 1] + f * (r.b[i] - r.b[i - 1]);
+            return a + b * k;
+        }
+    }
+    return (r.a[P - 1] + r.b[P - 1] * k) * (double)x / (double)kPerfN[P - 1];
+}
+
+// Predicted kernel time for `tiles` workgroups: full rounds of slots =
+// 256 CUs x workgroups per CU, then the last, partial round.
+double predict_us(const PerfRow &r, int wg_per_cu, int64_t tiles, int64_t K) {
+    const int64_t slots = (int64_t)kNumCU * (wg_per_cu > 0 ? wg_per_cu : 1);
+    const int64_t full = (tiles - 1) / slots;
+    const int64_t rem = tiles - full * slots;
+    return (double)full * perf_at(r, slots, K) + perf_at(r, rem, K);
+}
+
+// The SINGLE-variant table entry that names a tile shape (tile, waves).
+const KernelEntry *tile_entry(int dtype, int bm, int bn, int bkb, int waves) {
+    int count = 0;
+    const KernelEntry *table = tdg::kernel_table(&count);
+    for (int i = 0; i < count; i++) {
+        const KernelEntry &e = table[i];
+        if (e.dtype == dtype && !e.guard && e.variant == TDG_VARIANT_SINGLE && e.bm == bm &&
+            e.bn == bn && e.bkb == bkb && cfg_waves(e) == waves)
+            return &e;
+    }
     return nullptr;
 }
 
-// Tile shape for a product: the largest tile that still gives every compute
-// unit a workgroup; when no tile does, the one giving the most workgroups.
-// Skinny products (N <= 64) use the 64-column tiles.  Only the 128-byte K
-// tile is chosen automatically, with the measured wave count.
-const KernelEntry *choose_tile(int dtype, int64_t M, int64_t N, int64_t K, const tdg_config &req) {
+struct Choice {
+    const KernelEntry *tile;  // tile shape (its SINGLE entry)
+    int stages;               // ring depth for the direct-to-LDS loop; 0 = none measured
+};
+
+// Tile shape, waves and ring depth for a product: the measured configuration
+// with the least predicted time (a near tie, within 3%, goes to the earlier
+// row).  Requests outside the measured table (other K tiles, or a tile,
+// wave count or ring depth no row has) fall back to the largest tile that
+// gives every compute unit a workgroup, or the one giving the most.
+Choice choose_config(int dtype, int64_t M, int64_t N, int64_t K, const tdg_config &req) {
+    const PerfRow *best = nullptr;
+    const KernelEntry *best_tile = nullptr;
+    double best_t = 0.0;
+    const int es = elem_size(dtype);
+    const bool any_variant_ok = req.variant == TDG_VARIANT_AUTO || req.variant == TDG_VARIANT_DIRECT_LDS;
+    if (req.bk == 0 || req.bk * es == 128) {
+        for (const PerfRow &r : kPerf) {
+            if (r.dtype != dtype) continue;
+            if ((req.bm && req.bm != r.bm) || (req.bn && req.bn != r.bn) ||
+                (req.waves && req.waves != r.waves))
+                continue;
+            if (req.lds_stages && any_variant_ok && req.lds_stages != r.stages) continue;
+            const KernelEntry *t = tile_entry(dtype, r.bm, r.bn, 128, r.waves);
+            if (!t) continue;
+            tdg_plan_info fig;
+            tile_figures(dtype, r.bm, r.bn, 128 / es, r.waves, r.stages, TDG_VARIANT_DIRECT_LDS, M, N,
+                         K, &fig);
+            const double t_us = predict_us(r, fig.wg_per_cu, fig.grid, K);
+            if (!best || t_us < best_t * 0.97) {
+                best = &r;
+                best_tile = t;
+                best_t = t_us;
+            }
+        }
+    }
+    if (best) return Choice{best_tile, best->stages};
+
     int count = 0;
     const KernelEntry *table = tdg::kernel_table(&count);
-    const KernelEntry *best = nullptr;
+    const KernelEntry *pick = nullptr;
     int64_t best_area = -1, best_grid = -1;
     bool best_fills = false;
-    (void)K;
     for (int i = 0; i < count; i++) {
         const KernelEntry &e = table[i];
         if (e.dtype != dtype || e.guard || e.variant != TDG_VARIANT_SINGLE) continue;
         if (!tile_matches(req, e)) continue;
         if (req.bk == 0 && e.bkb != 128) continue;
-        if (req.waves == 0) {
-            const Measured *m = measured_for(e.bm, e.bn, e.bkb);
-            if (cfg_waves(e) != (m ? m->waves : 4)) continue;
-        }
-        if (req.bn == 0 && N <= 64 && e.bn != 64) continue;
         const int64_t grid = ceil_div(M, e.bm) * ceil_div(N, e.bn);
         const int64_t area = (int64_t)e.bm * e.bn;
         const bool fills = grid >= kNumCU;
         bool better;
-        if (!best) better = true;
+        if (!pick) better = true;
         else if (fills != best_fills) better = fills;
         else if (fills) better = area > best_area;
         else better = grid > best_grid || (grid == best_grid && area > best_area);
         if (better) {
-            best = &e;
+            pick = &e;
             best_area = area;
             best_grid = grid;
             best_fills = fills;
         }
     }
-    return best;
+    return Choice{pick, 0};
 }
 
 const KernelEntry *find_entry(const KernelEntry &tile, int stages, int variant, bool guard) {
@@ -286,16 +415,6 @@ const KernelEntry *find_entry(const KernelEntry &tile, int stages, int variant, 
             return &e;
     }
     return nullptr;
-}
-
-// Ring depth the direct-to-LDS loop uses when the caller leaves it open: the
-// measured best for the tile shape when it is built (in the plain or the
-// bounds-checked form, as asked), else two buffers.
-int preferred_direct_stages(const KernelEntry &tile, bool guard) {
-    const Measured *m = measured_for(tile.bm, tile.bn, tile.bkb);
-    if (m && m->waves == cfg_waves(tile) && find_entry(tile, m->stages, TDG_VARIANT_DIRECT_LDS, guard))
-        return m->stages;
-    return 2;
 }
 
 struct Resolved {
@@ -311,8 +430,17 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     tdg_config req = req_in;
     if (req.variant < 0 || req.variant > TDG_VARIANT_DIRECT_LDS) return TDG_ERR_INVALID_ARG;
     if (req.lds_stages < 0 || req.lds_stages > 8) return TDG_ERR_UNSUPPORTED;
-    const KernelEntry *tile = choose_tile(dtype, M, N, K, req);
+    const Choice choice = choose_config(dtype, M, N, K, req);
+    const KernelEntry *tile = choice.tile;
     if (!tile) return TDG_ERR_UNSUPPORTED;
+    // Ring depth of the direct-to-LDS loop when the caller leaves it open:
+    // the chosen configuration's, when it is built in the form asked for
+    // (plain or bounds-checked), else two buffers.
+    auto direct_stages = [&](bool guarded) {
+        if (choice.stages && find_entry(*tile, choice.stages, TDG_VARIANT_DIRECT_LDS, guarded))
+            return choice.stages;
+        return 2;
+    };
     const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
     const bool fast = fast_ok(*tile, M, N, K, vec_ok);
     const bool edge = !fast && edge_ok(*tile, N, K, vec_ok);
@@ -330,7 +458,7 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     if (stages == 0)
         stages = variant == TDG_VARIANT_SINGLE ? 1
                  : variant == TDG_VARIANT_REG_PREFETCH ? 2
-                                                       : preferred_direct_stages(*tile, !fast);
+                                                       : direct_stages(!fast);
     if (variant == TDG_VARIANT_SINGLE && stages != 1) return TDG_ERR_UNSUPPORTED;
     if (variant == TDG_VARIANT_REG_PREFETCH && stages > 2) return TDG_ERR_UNSUPPORTED;
     if (variant == TDG_VARIANT_DIRECT_LDS && stages < 2) return TDG_ERR_UNSUPPORTED;
@@ -349,7 +477,7 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         if (edge) {
             e = find_entry(*tile, stages, variant, true);
             if (!e) {
-                stages = preferred_direct_stages(*tile, true);
+                stages = direct_stages(true);
                 e = find_entry(*tile, stages, variant, true);
             }
             if (!e) {
