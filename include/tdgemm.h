@@ -179,8 +179,14 @@ int gemm_f32f32_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
 /* Planner.  Chooses the configuration the _pipelined call would run for this
  * dtype and shape (variant = TDG_VARIANT_AUTO), or, when `out` holds a
  * partly filled request on entry (any field non-zero), completes that
- * request.  Writes the result to *out and its figures to *info (either may be
- * NULL).  Host-only arithmetic: needs no device. */
+ * request.  Among the built direct-to-LDS configurations it takes the one
+ * with the least predicted kernel time, from a table of times measured on
+ * MI355X against workgroup count and K ("Pipeline GPU Kernel", Step 2: when
+ * the compute/load ratio does not settle the choice, build the candidates
+ * and measure them); a request outside that table gets the largest tile
+ * that still gives every compute unit a workgroup.  Writes the result to
+ * *out and its figures to *info (either may be NULL).  Host-only
+ * arithmetic: needs no device. */
 int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info);
 
 /* The planner's arithmetic for any tile, built or not: the compute/load
