@@ -176,6 +176,36 @@ int gemm_f32f32_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                    const float *B, int64_t ldb, float *C, int64_t ldc, void *stream,
                    const tdg_config *cfg);
 
+/* Split K ("Pipeline GPU Kernel", Step 1: too few tiles leave the loop's
+ * overlap, and here the chip, unused).  A product with few C tiles and a long
+ * K, say 256 x 256 x 65536, keeps one workgroup per tile and leaves most
+ * compute units idle.  These entry points cut K into `parts` slices of whole
+ * K tiles: parts workgroups per C tile each compute one slice's partial
+ * tile into `workspace`, and a second kernel sums the slices in slice order
+ * into C.  The result is deterministic, and exact for INT8.
+ *   parts == 0  the planner's choice (tdg_splitk_plan); 1 runs the plain
+ *               pipelined GEMM, for which the workspace may be NULL;
+ *   workspace   caller-owned device memory of at least parts * M * N * 4
+ *               bytes, 16-byte aligned, not overlapping A, B or C;
+ *               its contents on return are unspecified.
+ * A parts count above the number of K tiles is lowered to it.  Errors as for
+ * the other entry points; a missing or short workspace is
+ * TDG_ERR_INVALID_ARG.  The two kernels are enqueued on `stream`. */
+int gemm_f16f32_splitk(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb, float *C, int64_t ldc, int parts,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int gemm_i8i32_splitk(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
+                      const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, int parts,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int gemm_f32f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                       const float *B, int64_t ldb, float *C, int64_t ldc, int parts,
+                       void *workspace, size_t workspace_bytes, void *stream);
+/* The number of K parts the split-K entry points choose for this product (1
+ * when splitting is not predicted to be at least 10% faster) and the
+ * workspace they then need (0 for 1 part).  Host-only. */
+int tdg_splitk_plan(int dtype, int64_t M, int64_t N, int64_t K, int *parts,
+                    size_t *workspace_bytes);
+
 /* Planner.  Chooses the configuration the _pipelined call would run for this
  * dtype and shape (variant = TDG_VARIANT_AUTO), or, when `out` holds a
  * partly filled request on entry (any field non-zero), completes that

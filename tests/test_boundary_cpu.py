@@ -362,3 +362,29 @@ def test_planner_respects_partial_requests():
     assert _plan_str(F16, 2048, 2048, 2048, bm=128, bn=128, lds_stages=2) == "128x128 w4 s2 direct_lds"
     cfg, _ = tdg.tdg_plan(F16, 4096, 4096, 4096, cfg={"bk": 32})
     assert cfg["bk"] == 32 and cfg["bm"] == 256
+
+
+def test_splitk_plan_and_workspace_validation():
+    """Split K is planned only where tiles leave the chip idle, and its
+    workspace is checked before any HIP call: missing, short, misaligned or
+    overlapping A, B or C is TDG_ERR_INVALID_ARG (a good one reaches the
+    device check, TDG_ERR_NO_DEVICE here)."""
+    F16 = tdg.TDG_DTYPE_F16F32
+    parts, ws = tdg.tdg_splitk_plan(F16, 256, 256, 65536)
+    assert parts > 1 and ws == parts * 256 * 256 * 4
+    assert tdg.tdg_splitk_plan(F16, 4096, 4096, 4096) == (1, 0)
+    assert tdg.tdg_splitk_plan(F16, 256, 256, 0) == (1, 0)
+    lib = tdg.load_library()
+    M, N, K, P = 256, 256, 8192, 4
+    A, B, C, W = 1 << 40, 2 << 40, 3 << 40, 4 << 40
+    need = P * M * N * 4
+    call = lambda ws, nbytes, parts=P: lib.gemm_f16f32_splitk(M, N, K, A, K, B, N, C, N, parts, ws,
+                                                              nbytes, None)
+    assert call(W, need) == tdg.TDG_ERR_NO_DEVICE
+    assert call(None, need) == tdg.TDG_ERR_INVALID_ARG
+    assert call(W, need - 1) == tdg.TDG_ERR_INVALID_ARG
+    assert call(W + 4, need) == tdg.TDG_ERR_INVALID_ARG
+    assert call(C + 64, need) == tdg.TDG_ERR_INVALID_ARG      # overlaps C
+    assert call(A, need) == tdg.TDG_ERR_INVALID_ARG           # overlaps A
+    assert call(W, need, parts=-1) == tdg.TDG_ERR_INVALID_ARG
+    assert call(None, 0, parts=1) == tdg.TDG_ERR_NO_DEVICE    # one part needs no workspace

@@ -48,6 +48,7 @@ EXPORTED = (
     "tdg_plan", "tdg_tile_figures", "tdg_config_count",
     "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
+    "gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk", "tdg_splitk_plan",
 )
 
 
@@ -122,6 +123,13 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_status_string.restype = ctypes.c_char_p
     lib.tdg_set_debug_flags.argtypes = [c_int]
     lib.tdg_set_debug_flags.restype = c_int
+    for name in ("gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk"):
+        fn = getattr(lib, name)
+        fn.argtypes = gemm_args[:9] + [c_int, vp, ctypes.c_size_t, vp]
+        fn.restype = c_int
+    lib.tdg_splitk_plan.argtypes = [c_int, i64, i64, i64, ctypes.POINTER(c_int),
+                                    ctypes.POINTER(ctypes.c_size_t)]
+    lib.tdg_splitk_plan.restype = c_int
     lib.tdg_copy_f32.argtypes = [i64, i64, vp, i64, vp, i64, vp]
     lib.tdg_copy_f32.restype = c_int
     lib.tdg_transpose_f32.argtypes = [c_int, i64, i64, vp, i64, vp, i64, vp]
@@ -185,7 +193,7 @@ def _matrix(t, dtypes, what):
     return rows, cols, t.data_ptr(), max(ld, 1)
 
 
-def _gemm(name, A, B, C, cfg, f16):
+def _gemm(name, A, B, C, cfg, f16, splitk=None):
     """f16: True (binary16 in), False (int8 in) or "f32" (binary32 in)."""
     torch = _torch()
     if f16 == "f32":
@@ -206,14 +214,24 @@ def _gemm(name, A, B, C, cfg, f16):
         raise ValueError("C has shape %s, expected %s" % ((Mc, Nc), (M, N)))
     fn = _fn(name)
     tail = (ctypes.byref(cfg) if cfg is not None else None,) if name.endswith("_ex") else ()
+    mid = ()
+    if splitk is not None:  # (parts, workspace tensor or None)
+        parts, ws = splitk
+        if ws is None:
+            parts, need = (parts, parts * M * N * 4) if parts > 1 else tdg_splitk_plan(
+                {"gemm_f16f32_splitk": TDG_DTYPE_F16F32, "gemm_i8i32_splitk": TDG_DTYPE_I8I32,
+                 "gemm_f32f32_splitk": TDG_DTYPE_F32F32}[name], M, N, K)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=A.device) if parts > 1 else None
+        mid = (parts, ws.data_ptr() if ws is not None else None,
+               ws.numel() * ws.element_size() if ws is not None else 0)
     dev = A.device.index
     if dev is None or dev == torch.cuda.current_device():
         stream = torch.cuda.current_stream().cuda_stream
-        rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, stream, *tail)
+        rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, *mid, stream, *tail)
     else:
         with torch.cuda.device(A.device):
             stream = torch.cuda.current_stream(A.device).cuda_stream
-            rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, stream, *tail)
+            rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, *mid, stream, *tail)
     if rc != TDG_OK:
         raise TdgError(rc, name)
     return C
@@ -290,6 +308,31 @@ def tdg_tile_figures(dtype: int, bm: int, bn: int, bk: int, waves: int = 4, stag
     if rc != TDG_OK:
         raise TdgError(rc, "tdg_tile_figures")
     return info.as_dict()
+
+
+def tdg_splitk_plan(dtype: int, M: int, N: int, K: int):
+    """(parts, workspace bytes) the split-K entry points choose for this product."""
+    parts, ws = ctypes.c_int(), ctypes.c_size_t()
+    rc = load_library().tdg_splitk_plan(dtype, M, N, K, ctypes.byref(parts), ctypes.byref(ws))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_splitk_plan")
+    return parts.value, ws.value
+
+
+def gemm_f16f32_splitk(A, B, C=None, parts: int = 0, workspace=None):
+    """C (float32) = A . B (float16) with K split over `parts` (0: planner's
+    choice); the workspace is allocated here when not given."""
+    return _gemm("gemm_f16f32_splitk", A, B, C, None, True, splitk=(parts, workspace))
+
+
+def gemm_i8i32_splitk(A, B, C=None, parts: int = 0, workspace=None):
+    """C (int32) = A . B (int8) with K split over `parts`; exact."""
+    return _gemm("gemm_i8i32_splitk", A, B, C, None, False, splitk=(parts, workspace))
+
+
+def gemm_f32f32_splitk(A, B, C=None, parts: int = 0, workspace=None):
+    """C (float32) = A . B (float32) with K split over `parts`."""
+    return _gemm("gemm_f32f32_splitk", A, B, C, None, "f32", splitk=(parts, workspace))
 
 
 def tdg_set_debug_flags(flags: int) -> int:

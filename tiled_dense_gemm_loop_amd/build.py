@@ -32,6 +32,7 @@ UNITS = [
     ("tdg_api.hip", [], "tdg_api.o"),
     ("tdg_move.hip", [], "tdg_move.o"),
     ("tdg_probe.hip", [], "tdg_probe.o"),
+    ("tdg_reduce.hip", [], "tdg_reduce.o"),
 ]
 
 

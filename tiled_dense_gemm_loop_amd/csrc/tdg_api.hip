@@ -574,9 +574,11 @@ int resolve_cached(int dtype, int64_t M, int64_t N, int64_t K, const void *A, in
     return rc;
 }
 
+// Launch one GEMM.  With parts > 1 (split K), the kernel writes `parts`
+// dense M x N partial products to `ws` and a second kernel sums them into C.
 int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
         int64_t ldb, void *C, int64_t ldc, void *stream, const tdg_config *cfg,
-        bool pipelined_default) {
+        bool pipelined_default, int parts = 1, void *ws = nullptr) {
     int rc = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
     if (rc != TDG_OK) return rc;
     if (M == 0 || N == 0) return TDG_OK;
@@ -606,7 +608,18 @@ int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, 
     args.k_tiles = (int)ceil_div(K, cfg_bk(e));
     args.flags = tdg::debug_flags.load(std::memory_order_relaxed);
     args.k_rotate = k_rotation(dtype, N, K) && !(args.flags & TDG_DEBUG_NO_K_ROTATION) ? 1 : 0;
-    const int64_t grid = (int64_t)args.tiles_m * args.tiles_n;
+    // Split K only over whole tiles, and never into an empty part.
+    if (parts > args.k_tiles) parts = args.k_tiles > 0 ? args.k_tiles : 1;
+    args.k_per_part = parts > 1 ? (int)ceil_div(args.k_tiles, parts) : args.k_tiles;
+    if (parts > 1) parts = (int)ceil_div(args.k_tiles, args.k_per_part);
+    args.k_parts = parts;
+    args.part_stride = 0;
+    if (parts > 1) {
+        args.C = (unsigned char *)ws;
+        args.ldc = N;
+        args.part_stride = M * N * 4;
+    }
+    const int64_t grid = (int64_t)args.tiles_m * args.tiles_n * parts;
     if (grid > INT32_MAX) return TDG_ERR_UNSUPPORTED;
 
     void *kargs[] = {&args};
@@ -614,7 +627,101 @@ int run(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, 
                                      0, (hipStream_t)stream);
     if (err != hipSuccess) return TDG_ERR_LAUNCH;
     if (hipGetLastError() != hipSuccess) return TDG_ERR_LAUNCH;
+    if (parts > 1) return tdg::launch_sum_parts(dtype, parts, ws, M, N, C, ldc, stream);
     return TDG_OK;
+}
+
+// ---------------------------------------------------------------- split K
+
+// Predicted microseconds of the split-K second pass: read parts partial
+// products and write C at HBM speed, plus a launch.
+double sum_parts_us(int parts, int64_t M, int64_t N) {
+    const double bytes = (double)(parts + 1) * (double)M * (double)N * 4.0;
+    return 5.0 + bytes / 3.0e6;  // a launch and ~3 TB/s
+}
+
+// Split-K plan: the configuration and number of K parts with the least
+// predicted time, for products whose tiles leave most compute units idle.
+// parts = 1 (no split) unless splitting is predicted at least 10% faster.
+// Each part keeps at least two K tiles, so its loop still pipelines.
+int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, int *parts) {
+    tdg_config req;
+    memset(&req, 0, sizeof(req));
+    const Choice base = choose_config(dtype, M, N, K, req);
+    if (!base.tile) return TDG_ERR_UNSUPPORTED;
+    const int es = elem_size(dtype);
+    double best_t = -1.0;
+    const PerfRow *best_row = nullptr;
+    int best_parts = 1;
+    for (const PerfRow &r : kPerf) {
+        if (r.dtype != dtype || !tile_entry(dtype, r.bm, r.bn, 128, r.waves)) continue;
+        const int bk = 128 / es;
+        const int64_t k_tiles = ceil_div(K, bk);
+        tdg_plan_info fig;
+        tile_figures(dtype, r.bm, r.bn, bk, r.waves, r.stages, TDG_VARIANT_DIRECT_LDS, M, N, K, &fig);
+        for (int p = 1; p <= 256; p *= 2) {
+            if (p > 1 && k_tiles < 2 * p) break;
+            const int64_t per = ceil_div(k_tiles, p);
+            const int64_t used = ceil_div(k_tiles, per);
+            double t = predict_us(r, fig.wg_per_cu, fig.grid * used, per * bk);
+            if (used > 1) t += sum_parts_us((int)used, M, N);
+            if (best_t < 0.0 || t < best_t) {
+                best_t = t;
+                best_row = &r;
+                best_parts = (int)used;
+            }
+        }
+    }
+    // the plain plan's own prediction: keep it unless the split is clearly faster
+    double plain_t = -1.0;
+    for (const PerfRow &r : kPerf) {
+        if (r.dtype == dtype && r.bm == base.tile->bm && r.bn == base.tile->bn &&
+            r.waves == cfg_waves(*base.tile) && r.stages == base.stages) {
+            tdg_plan_info fig;
+            tile_figures(dtype, r.bm, r.bn, 128 / es, r.waves, r.stages, TDG_VARIANT_DIRECT_LDS, M, N, K,
+                         &fig);
+            plain_t = predict_us(r, fig.wg_per_cu, fig.grid, K);
+        }
+    }
+    memset(cfg, 0, sizeof(*cfg));
+    if (!best_row || best_parts == 1 || (plain_t > 0.0 && best_t > 0.9 * plain_t)) {
+        *parts = 1;
+        return TDG_OK;
+    }
+    cfg->bm = best_row->bm;
+    cfg->bn = best_row->bn;
+    cfg->bk = 128 / es;
+    cfg->waves = best_row->waves;
+    cfg->lds_stages = best_row->stages;
+    cfg->variant = TDG_VARIANT_AUTO;
+    *parts = best_parts;
+    return TDG_OK;
+}
+
+int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+               int64_t ldb, void *C, int64_t ldc, int parts, void *ws, size_t ws_bytes, void *stream) {
+    int rc = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+    if (rc != TDG_OK) return rc;
+    if (parts < 0) return TDG_ERR_INVALID_ARG;
+    tdg_config cfg;
+    memset(&cfg, 0, sizeof(cfg));
+    if (parts == 0) {
+        rc = splitk_choose(dtype, M, N, K, &cfg, &parts);
+        if (rc != TDG_OK) return rc;
+    }
+    if (parts <= 1 || M == 0 || N == 0 || K == 0)
+        return run(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, parts <= 1 && cfg.bm ? &cfg : nullptr,
+                   true);
+    // The workspace: parts dense M x N partial products, 16-byte aligned,
+    // apart from A, B and C.
+    const uint64_t need = (uint64_t)parts * (uint64_t)M * (uint64_t)N * 4u;
+    if (!ws || ws_bytes < need || (uintptr_t)ws % 16) return TDG_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    if (ranges_overlap((uintptr_t)ws, need, (uintptr_t)A, span_bytes(M, K, lda, es)) ||
+        ranges_overlap((uintptr_t)ws, need, (uintptr_t)B, span_bytes(K, N, ldb, es)) ||
+        ranges_overlap((uintptr_t)ws, need, (uintptr_t)C, span_bytes(M, N, ldc, 4)))
+        return TDG_ERR_INVALID_ARG;
+    return run(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg.bm ? &cfg : nullptr, true, parts, ws);
 }
 
 }  // namespace
@@ -727,6 +834,41 @@ int tdg_config_at(int dtype, int index, tdg_config *out) {
         n++;
     }
     return TDG_ERR_INVALID_ARG;
+}
+
+int tdg_splitk_plan(int dtype, int64_t M, int64_t N, int64_t K, int *parts, size_t *workspace_bytes) {
+    if (!dtype_ok(dtype) || !parts) return TDG_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return TDG_ERR_INVALID_ARG;
+    *parts = 1;
+    if (workspace_bytes) *workspace_bytes = 0;
+    if (M == 0 || N == 0 || K == 0) return TDG_OK;
+    tdg_config cfg;
+    const int rc = splitk_choose(dtype, M, N, K, &cfg, parts);
+    if (rc != TDG_OK) return rc;
+    if (workspace_bytes && *parts > 1) *workspace_bytes = (size_t)*parts * (size_t)M * (size_t)N * 4u;
+    return TDG_OK;
+}
+
+int gemm_f16f32_splitk(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B,
+                       int64_t ldb, float *C, int64_t ldc, int parts, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    return run_splitk(TDG_DTYPE_F16F32, M, N, K, A, lda, B, ldb, C, ldc, parts, workspace, workspace_bytes,
+                      stream);
+}
+
+int gemm_i8i32_splitk(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda, const int8_t *B,
+                      int64_t ldb, int32_t *C, int64_t ldc, int parts, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    return run_splitk(TDG_DTYPE_I8I32, M, N, K, A, lda, B, ldb, C, ldc, parts, workspace, workspace_bytes,
+                      stream);
+}
+
+int gemm_f32f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+                       int64_t ldb, float *C, int64_t ldc, int parts, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    return run_splitk(TDG_DTYPE_F32F32, M, N, K, A, lda, B, ldb, C, ldc, parts, workspace, workspace_bytes,
+                      stream);
 }
 
 int tdg_set_debug_flags(int flags) {

@@ -1,6 +1,8 @@
 // tdg_internal.h -- declarations shared by the kernel table and the host API.
 #pragma once
 
+#include <stdint.h>
+
 namespace tdg {
 
 // One built kernel: its tile shape, loop form and launch needs.
@@ -25,5 +27,11 @@ const KernelEntry *kernel_table(int *count);
 
 // TDG_OK when the current device is gfx950, else TDG_ERR_NO_DEVICE.
 int device_check();
+
+// Split-K second pass: C (M x N, ldc) = sum over `parts` dense M x N partial
+// products at ws, in part order.  FP32 for the FP16 / FP32 dtypes, INT32 for
+// INT8.  Enqueued on `stream`.
+int launch_sum_parts(int dtype, int parts, const void *ws, int64_t M, int64_t N, void *C, int64_t ldc,
+                     void *stream);
 
 }  // namespace tdg

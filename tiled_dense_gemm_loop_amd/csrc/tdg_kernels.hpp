@@ -74,6 +74,11 @@ struct GemmArgs {
     int k_tiles;  // ceil(K / BK); 0 when K == 0 (C is then zero-filled)
     int flags;    // TDG_DEBUG_* bits
     int k_rotate; // 1: tile row tm walks its K tiles from tm mod k_tiles
+    // Split K: k_parts workgroups per C tile, part p taking K tiles
+    // [p * k_per_part, min(k_tiles, (p + 1) * k_per_part)) and writing its
+    // partial tile at C + p * part_stride bytes.  k_parts == 1: plain GEMM.
+    int k_parts, k_per_part;
+    int64_t part_stride;
 };
 
 // Compile-time geometry of one configuration.
@@ -325,9 +330,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     const int wm = wave % WM, wn = wave / WM;
 
     int tm, tn;
-    map_tile(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
+    const int tile_id = (int)blockIdx.x / args.k_parts;
+    const int part = (int)blockIdx.x - tile_id * args.k_parts;
+    map_tile(tile_id, args.tiles_m, args.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nt = args.k_tiles;
+    const int kb = part * args.k_per_part;  // this workgroup's first K tile
+    const int nt = min(args.k_tiles - kb, args.k_per_part);
 
     // Race screen: with the debug flag set, the whole LDS ring is filled with
     // 0xFF bytes before the first tile is requested.  A fragment read of a
@@ -413,10 +421,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // HBM: without the rotation every workgroup reads the same K columns of
     // its rows at once, and with a row stride that is a multiple of the HBM
     // channel interleave those reads land on a few channels.  `kt` below is
-    // the position in the walk; phys() is the K tile it loads.  Every loop
-    // form uses the same walk, so their results stay bitwise identical.
+    // the position in the walk over this workgroup's nt tiles (its K part);
+    // phys() is the K tile it loads.  Every loop form uses the same walk, so
+    // their results stay bitwise identical.
     const int krot = args.k_rotate && nt > 0 ? tm % nt : 0;
-    auto phys = [&](int kt) { return kt + krot >= nt ? kt + krot - nt : kt + krot; };
+    auto phys = [&](int kt) { return kb + (kt + krot >= nt ? kt + krot - nt : kt + krot); };
     auto a_ptr = [&](int kt, int i) {
         return a_base + (int64_t)kt * G::BKB + (int64_t)(i * A_RSTEP) * lda_b;
     };
@@ -736,7 +745,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // streaming it past the L2 keeps the A and B lines that workgroups still
     // running read (FP16 / INT8 4096^3: about 1% faster).
     wait_vmcnt<0>();
-    out_t *C = (out_t *)args.C;
+    out_t *C = (out_t *)(args.C + (int64_t)part * args.part_stride);
     const int col_l = lane & 31, rq = (lane >> 5) * 4;
 #pragma unroll
     for (int mi = 0; mi < G::MI; mi++)
