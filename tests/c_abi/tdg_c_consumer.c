@@ -156,6 +156,32 @@ static int gpu_case(int dtype, int64_t M, int64_t N, int64_t K) {
                   sum[i]);
         }
     }
+    /* the same product with K split in 3 parts through a hipMalloc workspace:
+       INT8 must not change at all, the others stay within the bound */
+    if (K >= 3 * 128) {
+        void *ws = NULL;
+        const size_t wsb = (size_t)3 * (size_t)nc * 4u;
+        HIP_OK(hipMalloc(&ws, wsb));
+        HIP_OK(hipMemset(dc, 0, nc * 4));
+        if (dtype == TDG_DTYPE_I8I32)
+            rc = gemm_i8i32_splitk(M, N, K, da, K, db, N, dc, N, 3, ws, wsb, NULL);
+        else if (dtype == TDG_DTYPE_F16F32)
+            rc = gemm_f16f32_splitk(M, N, K, da, K, db, N, dc, N, 3, ws, wsb, NULL);
+        else
+            rc = gemm_f32f32_splitk(M, N, K, da, K, db, N, dc, N, 3, ws, wsb, NULL);
+        CHECK(rc == TDG_OK, "split-K gemm dtype %d: %s", dtype, tdg_status_string(rc));
+        HIP_OK(hipDeviceSynchronize());
+        HIP_OK(hipMemcpy(hc, dc, nc * 4, hipMemcpyDeviceToHost));
+        for (i = 0; i < nc; i++) {
+            if (dtype == TDG_DTYPE_I8I32) {
+                CHECK((int64_t)((int32_t *)hc)[i] == iref[i], "split-K int8 element %zu", i);
+            } else {
+                const double got = ((float *)hc)[i];
+                CHECK(fabs(got - ref[i]) <= 1e-4 * sum[i], "split-K element %zu: %.9g vs %.9g", i, got, ref[i]);
+            }
+        }
+        hipFree(ws);
+    }
     printf("gpu dtype %d %lldx%lldx%lld ok\n", dtype, (long long)M, (long long)N, (long long)K);
     hipFree(da);
     hipFree(db);
