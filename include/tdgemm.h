@@ -32,6 +32,7 @@
  * Argument rules (violations return TDG_ERR_INVALID_ARG before any HIP call):
  *   M, N, K >= 0;  lda >= max(1, K);  ldb >= max(1, N);  ldc >= max(1, N);
  *   a pointer may be NULL only when its matrix is empty;
+ *   rows * ld * sizeof(element) of each matrix must fit in int64;
  *   the bytes C spans may not overlap those of A or B.
  * Leading dimensions must also satisfy 64 * ld * sizeof(T) + 256 < 2^31 for
  * A and B (the kernels address 64 rows with 32-bit per-lane offsets): about
@@ -269,8 +270,9 @@ int tdg_set_debug_flags(int flags);
  *                 operands; other tiles take the LDS_SWIZZLED path).
  * AUTO is VEC.  Arguments: rows, cols >= 0 (and below 2^31 - 64);
  * ldi >= max(1, cols); ldo >= max(1, cols) for the copy and >= max(1, rows)
- * for the transpose (out is cols x rows); a pointer may be NULL only when the
- * matrix is empty; out may not overlap in.  Violations return
+ * for the transpose (out is cols x rows); rows * ld * 4 of each matrix must
+ * fit in int64; a pointer may be NULL only when the matrix is empty; out may
+ * not overlap in.  Violations return
  * TDG_ERR_INVALID_ARG before any HIP call; an empty matrix returns TDG_OK
  * with no launch; a non-gfx950 device returns TDG_ERR_NO_DEVICE; a failed
  * launch TDG_ERR_LAUNCH.  Asynchronous on `stream`, like the GEMM calls. */

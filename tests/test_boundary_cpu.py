@@ -51,6 +51,10 @@ BAD_CALLS = [
     ("C overlaps A", (4, 4, 4, 4096, 4, 1 << 20, 4, 4096 + 8, 4)),
     ("C overlaps B", (4, 4, 4, 1 << 20, 4, 8192, 4, 8192 - 16, 4)),
     ("M too large", (1 << 31, 4, 4, 4096, 4, 8192, 4, 1 << 40, 4)),
+    # rows x leading dimension past int64: no such matrix can exist
+    ("lda overflows", (4, 4, 4, 4096, 1 << 62, 1 << 40, 4, 1 << 44, 4)),
+    ("ldb overflows", (4, 4, 4, 4096, 4, 1 << 40, 1 << 62, 1 << 44, 4)),
+    ("ldc overflows", (4, 4, 4, 4096, 4, 1 << 40, 4, 1 << 44, 1 << 62)),
 ]
 
 
@@ -81,6 +85,8 @@ MOVE_BAD = [
     ("NULL out", (4, 4, 4096, 4, 0, 4)),
     ("out overlaps in", (4, 4, 4096, 4, 4096 + 32, 4)),
     ("rows too large", (1 << 31, 4, 4096, 4, 1 << 40, 4)),
+    ("ldi overflows", (4, 4, 4096, 1 << 62, 1 << 40, 4)),
+    ("ldo overflows", (4, 4, 4096, 4, 1 << 40, 1 << 62)),
 ]
 
 
@@ -127,6 +133,13 @@ def test_oversized_leading_dimension_is_unsupported():
                         1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
     assert tdg.call_raw("gemm_i8i32", 64, 64, 64, 1 << 30, 64, 1 << 40, 1 << 25,
                         1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
+    # a single row may have any leading dimension; one whose 64-row offset
+    # would wrap a 64-bit product must still be refused, not launched
+    for lda in (1 << 57, 1 << 59, (1 << 61) - 1):
+        assert tdg.call_raw("gemm_f16f32_pipelined", 1, 64, 64, 1 << 30, lda, 1 << 40, 64,
+                            1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
+    assert tdg.call_raw("gemm_i8i32_pipelined", 64, 1, 64, 1 << 30, 64, 1 << 40, 1 << 56,
+                        1 << 32, 1) == tdg.TDG_ERR_UNSUPPORTED
 
 
 def test_unbuilt_configuration_is_unsupported():

@@ -82,7 +82,15 @@ bool ranges_overlap(uintptr_t a0, uint64_t alen, uintptr_t b0, uint64_t blen) {
     return a0 < b0 + blen && b0 < a0 + alen;
 }
 
-// Bytes spanned by a rows x cols row-major matrix with leading dimension ld.
+// Whether rows x ld elements of es bytes fit in int64 (every matrix that can
+// exist does; a larger leading dimension is rejected before any arithmetic
+// on it could overflow).
+bool extent_ok(int64_t rows, int64_t ld, int es) {
+    return rows == 0 || ld <= INT64_MAX / es / rows;
+}
+
+// Bytes spanned by a rows x cols row-major matrix with leading dimension ld
+// (cols <= ld and extent_ok hold).
 uint64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
     if (rows == 0 || cols == 0) return 0;
     return (uint64_t)((rows - 1) * ld + cols) * (uint64_t)es;
@@ -99,6 +107,8 @@ int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t 
     if (K > 0 && N > 0 && !B) return TDG_ERR_INVALID_ARG;
     if (M > 0 && N > 0 && !C) return TDG_ERR_INVALID_ARG;
     const int es = elem_size(dtype);
+    if (!extent_ok(M, lda, es) || !extent_ok(K, ldb, es) || !extent_ok(M, ldc, 4))
+        return TDG_ERR_INVALID_ARG;
     const uint64_t cspan = span_bytes(M, N, ldc, 4);
     if (ranges_overlap((uintptr_t)C, cspan, (uintptr_t)A, span_bytes(M, K, lda, es)) ||
         ranges_overlap((uintptr_t)C, cspan, (uintptr_t)B, span_bytes(K, N, ldb, es)))
@@ -151,8 +161,8 @@ bool aligned_operands(int dtype, const void *A, int64_t lda, const void *B, int6
 // bytes; the planner refuses leading dimensions that would overflow them.
 bool offsets_fit(int dtype, int64_t lda, int64_t ldb) {
     const int64_t es = elem_size(dtype);
-    const int64_t lim = (int64_t)1 << 31;
-    return 64 * lda * es + 256 < lim && 64 * ldb * es + 256 < lim;
+    const int64_t max_ld = (((int64_t)1 << 31) - 257) / (64 * es);  // 64 ld es + 256 < 2^31
+    return lda <= max_ld && ldb <= max_ld;
 }
 
 // Estimated 32-bit registers per lane: accumulators, register staging of one

@@ -256,6 +256,9 @@ int launch_move(int method, bool transpose, int64_t rows, int64_t cols, const fl
     const int64_t out_cols = transpose ? rows : cols;
     const int64_t out_rows = transpose ? cols : rows;
     if (ldi < (cols > 1 ? cols : 1) || ldo < (out_cols > 1 ? out_cols : 1)) return TDG_ERR_INVALID_ARG;
+    // rows x leading dimension must fit in int64 bytes before span() uses it
+    if ((rows > 0 && ldi > INT64_MAX / 4 / rows) || (out_rows > 0 && ldo > INT64_MAX / 4 / out_rows))
+        return TDG_ERR_INVALID_ARG;
     if (rows > 0 && cols > 0 && (!in || !out)) return TDG_ERR_INVALID_ARG;
     if (overlap(in, span(rows, cols, ldi), out, span(out_rows, out_cols, ldo)))
         return TDG_ERR_INVALID_ARG;
