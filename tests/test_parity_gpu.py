@@ -667,6 +667,30 @@ def test_invalid_arguments_are_rejected(lib):
                         0, cfg) == lib.TDG_ERR_UNSUPPORTED
 
 
+def test_binding_rejects_host_tensors(lib):
+    """The binding passes device pointers only: an output, workspace or
+    copy destination in host memory is refused before the library is
+    called, and the output is left as it was."""
+    import torch
+    A = torch.ones((64, 64), dtype=torch.float16, device="cuda")
+    B = torch.ones((64, 64), dtype=torch.float16, device="cuda")
+    host_C = torch.full((64, 64), 7.0)
+    with pytest.raises(ValueError):
+        lib.gemm_f16f32_pipelined(A, B, host_C)
+    assert torch.all(host_C == 7.0)
+    with pytest.raises(ValueError):
+        lib.gemm_f16f32_pipelined(A.cpu(), B)
+    with pytest.raises(ValueError):
+        lib.gemm_f16f32_splitk(A, B, parts=2, workspace=torch.empty(2 * 64 * 64 * 4, dtype=torch.uint8))
+    ws = torch.empty(4 * 64 * 64 * 4, dtype=torch.uint8, device="cuda")[::2]  # not contiguous
+    with pytest.raises(ValueError):
+        lib.gemm_f16f32_splitk(A, B, parts=2, workspace=ws)
+    x = torch.ones((64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        lib.tdg_transpose_f32(x, out=torch.empty((64, 64)))
+    torch.cuda.synchronize()
+
+
 # --- the full-size workloads, in the configuration the benchmark times ---------------------
 
 @pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny", "fp32_4096"])

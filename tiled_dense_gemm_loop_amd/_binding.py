@@ -212,6 +212,8 @@ def _gemm(name, A, B, C, cfg, f16, splitk=None):
     Mc, Nc, pc, ldc = _matrix(C, (out_type,), "C")
     if (Mc, Nc) != (M, N):
         raise ValueError("C has shape %s, expected %s" % ((Mc, Nc), (M, N)))
+    if C.device != A.device:
+        raise ValueError("C is on %s, A and B on %s" % (C.device, A.device))
     fn = _fn(name)
     tail = (ctypes.byref(cfg) if cfg is not None else None,) if name.endswith("_ex") else ()
     mid = ()
@@ -222,6 +224,8 @@ def _gemm(name, A, B, C, cfg, f16, splitk=None):
                 {"gemm_f16f32_splitk": TDG_DTYPE_F16F32, "gemm_i8i32_splitk": TDG_DTYPE_I8I32,
                  "gemm_f32f32_splitk": TDG_DTYPE_F32F32}[name], M, N, K)
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=A.device) if parts > 1 else None
+        elif not ws.is_cuda or ws.device != A.device or not ws.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on %s" % A.device)
         mid = (parts, ws.data_ptr() if ws is not None else None,
                ws.numel() * ws.element_size() if ws is not None else 0)
     dev = A.device.index
@@ -370,6 +374,8 @@ def _move(x, out, transpose, method):
     orow, ocol, po, ldo = _matrix(out, (torch.float32,), "out")
     if (orow, ocol) != shape:
         raise ValueError("out has shape %s, expected %s" % ((orow, ocol), shape))
+    if out.device != x.device:
+        raise ValueError("out is on %s, in on %s" % (out.device, x.device))
     lib = load_library()
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream

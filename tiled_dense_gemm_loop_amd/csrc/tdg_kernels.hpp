@@ -44,6 +44,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 #include "tdgemm.h"
 
 namespace tdg {
@@ -517,20 +519,28 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     }
     const bool b_col_ok = n0 + b_c * EPC < args.N;
     const int a_kc = a_c * EPC;  // first k of this thread's A chunk within a tile
+    const uint64_t zero_addr = (uint64_t)(uintptr_t)tdg_zero16;
     auto issue_direct_one = [&](uint32_t st_off, int kt, int d) __attribute__((always_inline)) {
         kt = phys(kt);
         const uint32_t wbase = smem_addr + st_off + (uint32_t)wave * 1024u;
         if constexpr (GUARD) {
-            const unsigned char *src;
+            // Branch-free: the address is formed whether or not the chunk is
+            // inside, and a select (two v_cndmask) swaps in the zero block;
+            // the tests combine with bitwise & so that no short-circuit
+            // turns them into divergent branches around every DMA.
+            const int k_lim = args.K - kt * G::BK;  // k of this tile inside K
+            uint64_t src;
             uint32_t m0v;
             if (d < G::CA) {
-                const bool ok = ((a_rows_ok >> d) & 1u) && kt * G::BK + a_kc < args.K;
-                src = ok ? a_ptr(kt, d) + a_voff : (const unsigned char *)tdg_zero16;
+                const uint64_t p = (uint64_t)(uintptr_t)(a_ptr(kt, d) + a_voff);
+                const bool ok = (bool)((a_rows_ok >> d) & 1u) & (a_kc < k_lim);
+                src = ok ? p : zero_addr;
                 m0v = wbase + (uint32_t)(d * G::NT * 16);
             } else {
                 const int i = d - G::CA;
-                const bool ok = b_col_ok && kt * G::BK + i * B_RSTEP + b_k0 < args.K;
-                src = ok ? b_ptr(kt, i) + b_voff : (const unsigned char *)tdg_zero16;
+                const uint64_t p = (uint64_t)(uintptr_t)(b_ptr(kt, i) + b_voff);
+                const bool ok = b_col_ok & (i * B_RSTEP + b_k0 < k_lim);
+                src = ok ? p : zero_addr;
                 m0v = wbase + (uint32_t)(G::A_BYTES + i * G::NT * 16);
             }
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0v) : "memory");
@@ -769,21 +779,29 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // non-temporal: C is written once and not read back by this kernel, and
     // streaming it past the L2 keeps the A and B lines that workgroups still
     // running read (FP16 / INT8 4096^3: about 1% faster).
+    // A bounds-checked kernel stores interior tiles without the per-element
+    // test (a uniform branch), so only edge tiles pay for the masking.
     wait_vmcnt<0>();
     out_t *C = (out_t *)(args.C + (int64_t)part * args.part_stride);
     const int col_l = lane & 31, rq = (lane >> 5) * 4;
+    auto store_all = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mi = 0; mi < G::MI; mi++)
+        for (int mi = 0; mi < G::MI; mi++)
 #pragma unroll
-        for (int ni = 0; ni < G::NI; ni++) {
-            const int col = n0 + wn * G::WTN + ni * 32 + col_l;
+            for (int ni = 0; ni < G::NI; ni++) {
+                const int col = n0 + wn * G::WTN + ni * 32 + col_l;
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int row = m0 + wm * G::WTM + mi * 32 + (v >> 2) * 8 + rq + (v & 3);
-                if (!GUARD || (row < args.M && col < args.N))
-                    __builtin_nontemporal_store(acc[mi][ni][v], &C[(int64_t)row * args.ldc + col]);
+                for (int v = 0; v < 16; v++) {
+                    const int row = m0 + wm * G::WTM + mi * 32 + (v >> 2) * 8 + rq + (v & 3);
+                    if (!decltype(masked)::value || (row < args.M && col < args.N))
+                        __builtin_nontemporal_store(acc[mi][ni][v], &C[(int64_t)row * args.ldc + col]);
+                }
             }
-        }
+    };
+    if (!GUARD || (m0 + BM <= args.M && n0 + BN <= args.N))
+        store_all(std::false_type{});
+    else
+        store_all(std::true_type{});
 }
 
 }  // namespace tdg

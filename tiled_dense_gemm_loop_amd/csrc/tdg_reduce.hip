@@ -20,7 +20,7 @@ namespace {
 constexpr int THREADS = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T, typename V>
 __global__ void __launch_bounds__(THREADS) k_sum_parts(const T *__restrict__ ws, int parts, int M, int N,
@@ -61,7 +61,9 @@ int launch_sum_parts(int dtype, int parts, const void *ws, int64_t M, int64_t N,
     if (blocks < 1) blocks = 1;
     int m = (int)M, n = (int)N, v = vec ? 1 : 0;
     void *kargs[] = {&ws, &parts, &m, &n, &C, &ldc, &v};
-    const void *fn = dtype == TDG_DTYPE_I8I32 ? (const void *)&k_sum_parts<int32_t, i32x4>
+    // INT32 parts are summed as unsigned words: the same bits as the
+    // matrix cores' wrapping 32-bit accumulation, without signed overflow
+    const void *fn = dtype == TDG_DTYPE_I8I32 ? (const void *)&k_sum_parts<uint32_t, u32x4>
                                               : (const void *)&k_sum_parts<float, f32x4>;
     if (hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(THREADS), kargs, 0, (hipStream_t)stream) !=
         hipSuccess)
