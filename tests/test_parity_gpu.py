@@ -237,6 +237,28 @@ def test_ragged_direct_every_tile(lib, dtype):
 
 
 @pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_ragged_direct_long_k_every_ring(lib, dtype):
+    """A ragged, chunk-aligned shape with a partial last K tile and enough
+    K tiles that every ring depth runs interior workgroups on the plain DMA
+    first and switches to the bounds-checked DMA for the tail: every tile
+    and ring agree with the element-wise guarded loop bit for bit, and with
+    the oracle."""
+    import torch
+    M, N, K = 300, 272, 2000 if dtype != I8 else 4016
+    A, B = _operands(dtype, M, N, K, seed=97)
+    dA, dB = to_device(A), to_device(B)
+    for tile in _tiles(CODE[dtype]):
+        ref_out = None
+        for name, cfg in _variants(lib, dtype, tile):
+            C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+            if ref_out is None:
+                _check(dtype, C, A, B)
+                ref_out = C
+            else:
+                assert torch.equal(ref_out, C), "%s differs at tile %s" % (name, tile)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_ragged_direct_padded_rows(lib, dtype):
     """Leading dimensions wider than the matrix (still 16-byte multiples)
     on the ragged direct path: nothing past a row's K or N is used."""
@@ -583,7 +605,11 @@ def test_concurrent_streams_from_host_threads(lib):
 
 @pytest.mark.parametrize("dtype,M,N,K", [(F16, 2048, 64, 8192), (I8, 2048, 64, 8192),
                                          (F32, 1024, 64, 4096), (F16, 1000, 70, 4000),
-                                         (I8, 777, 100, 5000), (F16, 512, 512, 1024)])
+                                         (I8, 777, 100, 5000), (F16, 512, 512, 1024),
+                                         # bounds-checked DMA: the partial K tile sits at a
+                                         # different walk position in every tile row
+                                         (F16, 1000, 72, 4000), (I8, 777, 112, 5008),
+                                         (F32, 500, 68, 3000)])
 def test_k_rotation_against_the_plain_walk(lib, dtype, M, N, K):
     """Shapes whose B fits in L2 walk K from a per-tile-row offset.  The
     same call with the rotation switched off (debug flag) walks K from 0:

@@ -27,7 +27,8 @@ namespace tdg {
 
 // Deeper direct-to-LDS rings where the LDS budget allows.
 #define TDG_DIRECT(DT, BM, BN, BKB, WM, WN, ST) TDG_ENTRY(DT, BM, BN, BKB, WM, WN, ST, VAR_DIRECT, false)
-// ... and their bounds-checked forms for the rings the planner picks.
+// ... and their bounds-checked forms, for every ring the planner's table
+// can pick, so that a ragged shape keeps the ring of its aligned neighbour.
 #define TDG_DIRECT_G(DT, BM, BN, BKB, WM, WN, ST) TDG_ENTRY(DT, BM, BN, BKB, WM, WN, ST, VAR_DIRECT, true)
 
 #define TDG_SHAPES(DT)                                                                   \
@@ -36,12 +37,14 @@ namespace tdg {
         TDG_DIRECT(DT, 256, 256, 64, 2, 2, 4), TDG_SHAPE(DT, 256, 256, 64, 2, 4),        \
         TDG_DIRECT(DT, 256, 256, 64, 2, 4, 3), TDG_DIRECT(DT, 256, 256, 64, 2, 4, 4),    \
         TDG_SHAPE(DT, 256, 128, 128, 2, 2), TDG_DIRECT(DT, 256, 128, 128, 2, 2, 3),      \
-        TDG_SHAPE(DT, 128, 128, 128, 2, 2), TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3),      \
-        TDG_DIRECT(DT, 128, 128, 128, 2, 2, 4), TDG_SHAPE(DT, 128, 64, 128, 4, 1),       \
-        TDG_DIRECT(DT, 128, 64, 128, 4, 1, 4), TDG_DIRECT(DT, 128, 64, 128, 4, 1, 6),    \
-        TDG_DIRECT_G(DT, 128, 64, 128, 4, 1, 4), TDG_SHAPE(DT, 64, 64, 128, 2, 2),       \
+        TDG_DIRECT_G(DT, 256, 128, 128, 2, 2, 3), TDG_SHAPE(DT, 128, 128, 128, 2, 2),    \
+        TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3), TDG_DIRECT(DT, 128, 128, 128, 2, 2, 4),  \
+        TDG_DIRECT_G(DT, 128, 128, 128, 2, 2, 3), TDG_DIRECT_G(DT, 128, 128, 128, 2, 2, 4), \
+        TDG_SHAPE(DT, 128, 64, 128, 4, 1), TDG_DIRECT(DT, 128, 64, 128, 4, 1, 4),        \
+        TDG_DIRECT(DT, 128, 64, 128, 4, 1, 6), TDG_DIRECT_G(DT, 128, 64, 128, 4, 1, 4),  \
+        TDG_DIRECT_G(DT, 128, 64, 128, 4, 1, 6), TDG_SHAPE(DT, 64, 64, 128, 2, 2),       \
         TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4), TDG_DIRECT(DT, 64, 64, 128, 2, 2, 8),      \
-        TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 4)
+        TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 4), TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 8)
 
 // FP32 inputs: v_mfma_f32_32x32x2_f32 does 8x fewer operations per byte of
 // LDS traffic than the FP16 MFMA, so the shapes are the same tiles with fewer
@@ -49,7 +52,7 @@ namespace tdg {
 // registers plus four MFMAs per K step per block spill.
 #define TDG_SHAPES_F32(DT)                                                                \
     TDG_SHAPE(DT, 256, 256, 128, 2, 4), TDG_SHAPE(DT, 128, 128, 128, 2, 2),              \
-        TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3),                                          \
+        TDG_DIRECT(DT, 128, 128, 128, 2, 2, 3), TDG_DIRECT_G(DT, 128, 128, 128, 2, 2, 3), \
         TDG_SHAPE(DT, 128, 64, 128, 4, 1), TDG_DIRECT(DT, 128, 64, 128, 4, 1, 4),        \
         TDG_DIRECT_G(DT, 128, 64, 128, 4, 1, 4), TDG_SHAPE(DT, 64, 64, 128, 2, 2),       \
         TDG_DIRECT(DT, 64, 64, 128, 2, 2, 4), TDG_DIRECT_G(DT, 64, 64, 128, 2, 2, 4)

@@ -504,12 +504,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // inline assembly so that the compiler does not guard the other buffer's
     // LDS reads with a wait on these copies; completion is awaited
     // explicitly (vmcnt) before the barrier that publishes the tile.
-    // Bounds-checked DMA (GUARD): the operands are 16-byte aligned with K and
-    // N whole 16-byte chunks, so a chunk is either wholly inside its matrix or
-    // wholly outside; one outside (A row >= M, k >= K; B row k >= K, column
-    // >= N) is fetched from the zero block instead.  The source is then a
-    // per-lane 64-bit address.  B columns >= N and A rows >= M only feed C
-    // elements that are never stored; k >= K must be zero.
+    // Bounds-checked DMA (GUARD, with the `checked` tag set): the operands are
+    // 16-byte aligned with K and N whole 16-byte chunks, so a chunk is either
+    // wholly inside its matrix or wholly outside; one outside (A row >= M,
+    // k >= K; B row k >= K, column >= N) is fetched from the zero block
+    // instead.  The source is then a per-lane 64-bit address.  B columns >= N
+    // and A rows >= M only feed C elements that are never stored; k >= K must
+    // be zero.  A bounds-checked kernel issues the plain form (wave-uniform
+    // base, 32-bit lane offset) for every K tile known to lie wholly inside
+    // the operands, so only edge workgroups and the K tail pay for checks.
     constexpr int EPC = 16 / G::ES;
     uint32_t a_rows_ok = 0;
     if constexpr (GUARD) {
@@ -520,10 +523,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     const bool b_col_ok = n0 + b_c * EPC < args.N;
     const int a_kc = a_c * EPC;  // first k of this thread's A chunk within a tile
     const uint64_t zero_addr = (uint64_t)(uintptr_t)tdg_zero16;
-    auto issue_direct_one = [&](uint32_t st_off, int kt, int d) __attribute__((always_inline)) {
+    auto issue_direct_one = [&](uint32_t st_off, int kt, int d, auto checked) __attribute__((always_inline)) {
         kt = phys(kt);
         const uint32_t wbase = smem_addr + st_off + (uint32_t)wave * 1024u;
-        if constexpr (GUARD) {
+        if constexpr (GUARD && decltype(checked)::value) {
             // Branch-free: the address is formed whether or not the chunk is
             // inside, and a select (two v_cndmask) swaps in the zero block;
             // the tests combine with bitwise & so that no short-circuit
@@ -546,6 +549,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0v) : "memory");
             return;
         }
+        // the tile index is wave-uniform; the bounds-checked kernels' uniformity
+        // analysis does not see it, and the base address must be scalar
+        if constexpr (GUARD) kt = __builtin_amdgcn_readfirstlane(kt);
         if (d < G::CA) {
             const uint32_t m0v = wbase + (uint32_t)(d * G::NT * 16);
             asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(a_voff), "s"(a_ptr(kt, d)),
@@ -559,9 +565,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                          : "memory");
         }
     };
-    auto issue_direct = [&](uint32_t st_off, int kt) __attribute__((always_inline)) {
+    auto issue_direct = [&](uint32_t st_off, int kt, auto checked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int d = 0; d < G::CA + G::CB; d++) issue_direct_one(st_off, kt, d);
+        for (int d = 0; d < G::CA + G::CB; d++) issue_direct_one(st_off, kt, d, checked);
     };
 
     // MFMA tile micro-kernel over one LDS buffer.  The fragments of K step
@@ -609,7 +615,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // With SUB > 1 (FP32) the step's MFMAs go round-robin over the
     // accumulators, so dependent MFMAs are NM instructions apart.
     auto step = [&](int cset, const unsigned char *rst, int rstep, int rset, bool reads,
-                    uint32_t dma_st, int dma_kt, bool dma, unsigned char *wst) {
+                    uint32_t dma_st, int dma_kt, bool dma, unsigned char *wst, auto checked) {
         constexpr int NM = G::MI * G::NI, NR = G::MI + G::NI, ND = G::CA + G::CB;
         constexpr int NMF = NM * MM::SUB;  // MFMA issue slots in the step
 #pragma unroll
@@ -631,7 +637,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             if (dma) {
 #pragma unroll
                 for (int d = (t * ND + NMF - 1) / NMF; d < ((t + 1) * ND + NMF - 1) / NMF; d++)
-                    issue_direct_one(dma_st, dma_kt, d);
+                    issue_direct_one(dma_st, dma_kt, d, checked);
             }
             if constexpr (VAR == VAR_REG) {
                 if (wst) {
@@ -666,7 +672,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     int dma_tile = 0;
     uint32_t dma_off = 0;
     unsigned char *early_st = nullptr;
-    auto compute_tile = [&](const unsigned char *st, auto &&boundary) {
+    auto compute_tile = [&](const unsigned char *st, auto &&boundary, auto checked) {
         const unsigned char *next = st;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; s++) {
@@ -675,9 +681,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             const unsigned char *rst = r < G::KSTEPS ? st : next;
             const int rstep = r < G::KSTEPS ? r : r - G::KSTEPS;
             step(set_of(s), rst, rstep, set_of(rstep), true, dma_off, dma_tile,
-                 VAR == VAR_DIRECT && r == G::KSTEPS, s == G::KSTEPS - 2 ? early_st : nullptr);
+                 VAR == VAR_DIRECT && r == G::KSTEPS, s == G::KSTEPS - 2 ? early_st : nullptr,
+                 checked);
         }
     };
+    using unchecked_t = std::false_type;
+    using checked_t = std::true_type;
     auto buf = [&](int t) { return smem + (t % STAGES) * G::STAGE_BYTES; };
 
     // ---- K loop ------------------------------------------------------------
@@ -694,7 +703,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 store_regs(smem);
                 __syncthreads();
                 read_first(smem);
-                compute_tile(smem, [&]() -> const unsigned char * { return smem; });
+                compute_tile(smem, [&]() -> const unsigned char * { return smem; }, unchecked_t{});
             }
         } else if constexpr (VAR == VAR_REG) {
             // Prologue: tile 0 into buffer 0.
@@ -719,7 +728,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                         __syncthreads();  // drained tile visible to every wave
                     }
                     return buf(t + 1);
-                });
+                }, unchecked_t{});
             }
         } else {
             // Ring of STAGES buffers, AHEAD = STAGES - 1 tiles in flight.
@@ -736,33 +745,65 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             static_assert((AHEAD - 1) * IPT <= 63, "vmcnt holds at most 63");
             auto stage_off = [&](int t) { return (uint32_t)((t % STAGES) * G::STAGE_BYTES); };
             auto src_tile = [&](int t) { return t < nt ? t : nt - 1; };
+            // Walk positions from `w_chk` on take the bounds-checked DMA: all
+            // of them in an edge workgroup (its tile crosses M or N), else
+            // those from the partial last K tile on (K not a whole number of
+            // tiles), else none.  Positions after a rotated walk wraps past
+            // the partial tile are whole again but stay checked.
+            int w_chk = nt;
+            if constexpr (GUARD) {
+                const int last = args.k_tiles - 1;  // the only tile that can be partial
+                if (m0 + BM > args.M || n0 + BN > args.N) {
+                    w_chk = 0;
+                } else if (args.K % G::BK != 0 && last >= kb && last < kb + nt) {
+                    const int w = last - kb - krot;
+                    w_chk = w < 0 ? w + nt : w;
+                }
+            }
+            auto issue_pos = [&](uint32_t off, int w) __attribute__((always_inline)) {
+                if (w >= w_chk) issue_direct(off, w, checked_t{});
+                else issue_direct(off, w, unchecked_t{});
+            };
             // Prologue: tiles 0 .. AHEAD-1 in flight, tile 0 published, tile
             // AHEAD issued into the still unused last buffer.
 #pragma unroll
-            for (int p = 0; p < AHEAD; p++) issue_direct(stage_off(p), src_tile(p));
+            for (int p = 0; p < AHEAD; p++) issue_pos(stage_off(p), src_tile(p));
             wait_vmcnt<(AHEAD - 1) * IPT>();
             __syncthreads();
-            issue_direct(stage_off(AHEAD), src_tile(AHEAD));
+            issue_pos(stage_off(AHEAD), src_tile(AHEAD));
             read_first(buf(0));
             // Main loop and epilogue (from tile nt - AHEAD on, the issued
-            // loads are the harmless repeats).
-            for (int t = 0; t < nt; t++) {
-                compute_tile(buf(t), [&]() -> const unsigned char * {
-                    if (t + 1 < nt) {
-                        wait_vmcnt<(AHEAD - 1) * IPT>();  // tile t+1 landed
-                        __syncthreads();
-                        dma_tile = src_tile(t + 1 + AHEAD);  // issued between this step's MFMAs
-                        dma_off = stage_off(t + 1 + AHEAD);
-                    } else {
-                        // last tile: no barrier; the repeat load goes to the
-                        // buffer of tile t - 1, which every wave has finished
-                        // reading (certified by the previous barrier) and
-                        // which is never read again
-                        dma_tile = nt - 1;
-                        dma_off = stage_off(t - 1 + STAGES);
-                    }
-                    return buf(t + 1);
-                });
+            // loads are the harmless repeats).  The DMA interleaved with tile
+            // t is for walk position min(t + 1 + AHEAD, nt - 1), which grows
+            // with t, so the loop runs in two parts: plain DMA up to t_chk,
+            // checked DMA from there (one copy of the loop in an unguarded
+            // kernel).
+            auto run_tiles = [&](int t0, int t1, auto checked) __attribute__((always_inline)) {
+                for (int t = t0; t < t1; t++) {
+                    compute_tile(buf(t), [&]() -> const unsigned char * {
+                        if (t + 1 < nt) {
+                            wait_vmcnt<(AHEAD - 1) * IPT>();  // tile t+1 landed
+                            __syncthreads();
+                            dma_tile = src_tile(t + 1 + AHEAD);  // issued between this step's MFMAs
+                            dma_off = stage_off(t + 1 + AHEAD);
+                        } else {
+                            // last tile: no barrier; the repeat load goes to
+                            // the buffer of tile t - 1, which every wave has
+                            // finished reading (certified by the previous
+                            // barrier) and which is never read again
+                            dma_tile = nt - 1;
+                            dma_off = stage_off(t - 1 + STAGES);
+                        }
+                        return buf(t + 1);
+                    }, checked);
+                }
+            };
+            if constexpr (GUARD) {
+                const int t_chk = w_chk >= nt ? nt : max(0, w_chk - 1 - AHEAD);
+                run_tiles(0, t_chk, unchecked_t{});
+                run_tiles(t_chk, nt, checked_t{});
+            } else {
+                run_tiles(0, nt, unchecked_t{});
             }
             // Drain the repeat loads before the workgroup ends: LDS written by
             // a DMA still in flight could otherwise land in the next
