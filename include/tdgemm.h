@@ -30,7 +30,8 @@
  * thread-safe.
  *
  * Argument rules (violations return TDG_ERR_INVALID_ARG before any HIP call):
- *   M, N, K >= 0;  lda >= max(1, K);  ldb >= max(1, N);  ldc >= max(1, N);
+ *   0 <= M, N, K <= 2^31 - 2^16 (the kernels index in 32 bits);
+ *   lda >= max(1, K);  ldb >= max(1, N);  ldc >= max(1, N);
  *   a pointer may be NULL only when its matrix is empty;
  *   rows * ld * sizeof(element) of each matrix must fit in int64;
  *   the bytes C spans may not overlap those of A or B.

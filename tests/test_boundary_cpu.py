@@ -51,6 +51,10 @@ BAD_CALLS = [
     ("C overlaps A", (4, 4, 4, 4096, 4, 1 << 20, 4, 4096 + 8, 4)),
     ("C overlaps B", (4, 4, 4, 1 << 20, 4, 8192, 4, 8192 - 16, 4)),
     ("M too large", (1 << 31, 4, 4, 4096, 4, 8192, 4, 1 << 40, 4)),
+    # sizes keep a 2^16 margin below 2^31 (tile start + extent in 32 bits)
+    ("M past the margin", ((1 << 31) - (1 << 16) + 1, 4, 4, 4096, 4, 8192, 4, 1 << 40, 4)),
+    ("N past the margin", (4, (1 << 31) - 1, 4, 4096, 4, 1 << 36, (1 << 31) - 1, 1 << 40, (1 << 31) - 1)),
+    ("K past the margin", (4, 4, (1 << 31) - 100, 4096, (1 << 31) - 100, 1 << 36, 4, 1 << 40, 4)),
     # rows x leading dimension past int64: no such matrix can exist
     ("lda overflows", (4, 4, 4, 4096, 1 << 62, 1 << 40, 4, 1 << 44, 4)),
     ("ldb overflows", (4, 4, 4, 4096, 4, 1 << 40, 1 << 62, 1 << 44, 4)),
@@ -401,3 +405,18 @@ def test_splitk_plan_and_workspace_validation():
     assert call(A, need) == tdg.TDG_ERR_INVALID_ARG           # overlaps A
     assert call(W, need, parts=-1) == tdg.TDG_ERR_INVALID_ARG
     assert call(None, 0, parts=1) == tdg.TDG_ERR_NO_DEVICE    # one part needs no workspace
+
+
+def test_sizes_keep_a_margin_below_2_31():
+    """The kernels form tile start + tile extent in 32 bits, so M, N and K
+    stop 2^16 short of 2^31: planning M at the limit works (a dense N or K
+    that large already breaks the leading-dimension limit), one past it is an
+    argument error for the planners and every entry point."""
+    lim = (1 << 31) - (1 << 16)
+    tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, lim, 64, 64)
+    tdg.tdg_plan(tdg.TDG_DTYPE_I8I32, lim, 64, 4096)
+    for args in ((lim + 1, 64, 64), (64, lim + 1, 64), (64, 64, lim + 1)):
+        with pytest.raises(tdg.TdgError):
+            tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, *args)
+        with pytest.raises(tdg.TdgError):
+            tdg.tdg_splitk_plan(tdg.TDG_DTYPE_I8I32, *args)

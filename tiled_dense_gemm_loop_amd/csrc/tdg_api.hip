@@ -71,6 +71,15 @@ int elem_size(int dtype) {
     return dtype == TDG_DTYPE_F16F32 ? 2 : (dtype == TDG_DTYPE_I8I32 ? 1 : 4);
 }
 
+// Largest M, N or K: the kernels index rows, columns and k in 32 bits and
+// form sums such as (tile start + tile extent) on them, so every size keeps a
+// margin of 2^16 below 2^31.
+constexpr int64_t kMaxDim = ((int64_t)1 << 31) - ((int64_t)1 << 16);
+
+bool dims_ok(int64_t M, int64_t N, int64_t K) {
+    return M >= 0 && N >= 0 && K >= 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
+}
+
 bool dtype_ok(int dtype) {
     return dtype == TDG_DTYPE_F16F32 || dtype == TDG_DTYPE_I8I32 || dtype == TDG_DTYPE_F32F32;
 }
@@ -99,8 +108,7 @@ uint64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
 int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
              int64_t ldb, const void *C, int64_t ldc) {
     if (!dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
-    if (M < 0 || N < 0 || K < 0) return TDG_ERR_INVALID_ARG;
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return TDG_ERR_INVALID_ARG;
+    if (!dims_ok(M, N, K)) return TDG_ERR_INVALID_ARG;
     if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
         return TDG_ERR_INVALID_ARG;
     if (M > 0 && K > 0 && !A) return TDG_ERR_INVALID_ARG;
@@ -795,8 +803,7 @@ int gemm_f32f32_ex(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
 
 int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info) {
     if (!dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
-    if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
-        return TDG_ERR_INVALID_ARG;
+    if (!dims_ok(M, N, K)) return TDG_ERR_INVALID_ARG;
     tdg_config req;
     memset(&req, 0, sizeof(req));
     if (out) req = *out;
@@ -848,8 +855,7 @@ int tdg_config_at(int dtype, int index, tdg_config *out) {
 
 int tdg_splitk_plan(int dtype, int64_t M, int64_t N, int64_t K, int *parts, size_t *workspace_bytes) {
     if (!dtype_ok(dtype) || !parts) return TDG_ERR_INVALID_ARG;
-    if (M < 0 || N < 0 || K < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
-        return TDG_ERR_INVALID_ARG;
+    if (!dims_ok(M, N, K)) return TDG_ERR_INVALID_ARG;
     *parts = 1;
     if (workspace_bytes) *workspace_bytes = 0;
     if (M == 0 || N == 0 || K == 0) return TDG_OK;
