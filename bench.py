@@ -82,6 +82,10 @@ def parse():
     p.add_argument("--no-ladder", action="store_true", help="skip the copy/transpose ladder")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured MFMA ceilings (MFMA-only probe)")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the FP16 4096^3 sweep over every built configuration")
+    p.add_argument("--sweep-steps", type=int, default=50,
+                   help="timed launches per configuration in the sweep")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -196,7 +200,7 @@ def cold_launches(tdg, wl, count: int = 20, scrub_mib: int = 512) -> dict:
     A, B, dA, dB, C = device_operands(wl)
     run = launcher(tdg, wl, dA, dB, C, "pipelined")
     scrub = torch.ones(scrub_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
-    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")  # the 0-d sum of the scrub
     run()
     out = {"workload": wl.name, "scrub_mib": scrub_mib, "count": count}
     for mode in ("read", "write"):
@@ -283,6 +287,39 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def tile_sweep(tdg, steps: int, warmup: int):
+    """FP16 4096^3 on every built configuration (tile, waves, LDS ring, loop
+    form): the planner's LDS budget, ratio and occupancy arithmetic
+    ("Pipeline GPU Kernel", Step 1 and Step 2; "Analyze Kernel Bottleneck",
+    Step 3 and Step 6) beside the runtime's view of the same kernel
+    (registers, spills, LDS, resident workgroups per CU), with the rate each
+    one reaches and its fraction of the dense MFMA peak."""
+    import torch
+    wl = si.WORKLOADS["fp16_4096"]
+    _, _, dA, dB, C = device_operands(wl)
+    code = DTYPE_CODE["f16"]
+    rows = []
+    for i in range(tdg.tdg_config_count(code)):
+        cfg = tdg.tdg_config_at(code, i)
+        res = tdg.tdg_config_resources(code, i)
+        fig = tdg.tdg_tile_figures(code, cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"],
+                                   cfg["lds_stages"], cfg["variant"], wl.M, wl.N, wl.K)
+        ms = time_launches(lambda: tdg.gemm_f16f32_ex(dA, dB, C, cfg=cfg), steps, warmup)
+        tf = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+        rows.append({
+            "tile": "%dx%dx%d" % (cfg["bm"], cfg["bn"], cfg["bk"]), "waves": cfg["waves"],
+            "lds_stages": cfg["lds_stages"], "variant": tdg.VARIANT_NAMES[cfg["variant"]],
+            "ratio": round(fig["ratio"], 1), "need_bytes_per_clk": round(fig["need_bytes_per_clk"], 1),
+            "lds_kib": round(fig["lds_bytes"] / 1024.0, 1), "grid": fig["grid"],
+            "wg_per_cu_planned": fig["wg_per_cu"], "wg_per_cu_runtime": res["wg_per_cu"],
+            "vgprs": res["vgprs"], "spill_bytes": res["spill_bytes"],
+            "us": round(ms * 1e3, 2), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK["f16"], 4)})
+    del dA, dB, C
+    torch.cuda.empty_cache()
+    rows.sort(key=lambda r: -r["tflops"])
+    return rows
 
 
 def cpu_baseline(wl, A, B, target_s: float):
@@ -372,6 +409,12 @@ def main():
                 del a, b, da, db, c
                 torch.cuda.empty_cache()
 
+    sweep = None
+    if not args.no_sweep:
+        sweep = tile_sweep(tdg, args.sweep_steps, max(1, args.sweep_steps // 5))
+        for r in sweep:
+            print("# sweep fp16 4096^3 %s" % json.dumps(r), file=sys.stderr, flush=True)
+
     cold = None if args.no_table else cold_launches(tdg, si.WORKLOADS["fp16_skinny"])
     if cold:
         print("# cold (512 MiB scrub before each launch) %s" % json.dumps(cold), file=sys.stderr,
@@ -460,6 +503,7 @@ def main():
         "cpu_baseline": cpu,
         "variants": table or None,
         "transpose_ladder": ladder,
+        "tile_sweep": sweep,
     }
     print(json.dumps(line), flush=True)
 

@@ -236,6 +236,24 @@ int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, i
 int tdg_config_count(int dtype);
 int tdg_config_at(int dtype, int index, tdg_config *out);
 
+/* What the i-th built-in configuration (numbered as by tdg_config_at) costs
+ * on the device, as the HIP runtime reports it for its kernel: the measured
+ * side of the LDS-budget / occupancy table that tdg_tile_figures predicts
+ * ("Analyze Kernel Bottleneck", Step 3 and Step 6: occupancy is limited by
+ * LDS, registers and wave slots).
+ *   vgprs       -- numRegs of the kernel's attributes (registers per lane);
+ *   spill_bytes -- private memory per lane (register spills; 0 when none);
+ *   lds_bytes   -- static LDS per workgroup (the ring of lds_stages tiles);
+ *   threads     -- workgroup size;
+ *   wg_per_cu   -- workgroups resident per compute unit by the runtime's
+ *                  occupancy calculation.
+ * Needs a gfx950 device (TDG_ERR_NO_DEVICE otherwise); a bad dtype, index or
+ * NULL out is TDG_ERR_INVALID_ARG; a failing runtime query TDG_ERR_LAUNCH. */
+typedef struct {
+    int vgprs, spill_bytes, lds_bytes, threads, wg_per_cu;
+} tdg_kernel_resources;
+int tdg_config_resources(int dtype, int index, tdg_kernel_resources *out);
+
 /* Human-readable name of a status code (static storage). */
 const char *tdg_status_string(int status);
 

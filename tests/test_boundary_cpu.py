@@ -420,3 +420,16 @@ def test_sizes_keep_a_margin_below_2_31():
             tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, *args)
         with pytest.raises(tdg.TdgError):
             tdg.tdg_splitk_plan(tdg.TDG_DTYPE_I8I32, *args)
+
+
+def test_config_resources_validation():
+    """tdg_config_resources: bad dtype, index or output are argument errors
+    before any HIP call; a valid query needs the gfx950 device."""
+    lib = tdg.load_library()
+    r = tdg.TdgKernelResources()
+    n = tdg.tdg_config_count(tdg.TDG_DTYPE_F16F32)
+    assert lib.tdg_config_resources(7, 0, ctypes.byref(r)) == tdg.TDG_ERR_INVALID_ARG
+    assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, -1, ctypes.byref(r)) == tdg.TDG_ERR_INVALID_ARG
+    assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, n, ctypes.byref(r)) == tdg.TDG_ERR_INVALID_ARG
+    assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, 0, None) == tdg.TDG_ERR_INVALID_ARG
+    assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, 0, ctypes.byref(r)) == tdg.TDG_ERR_NO_DEVICE

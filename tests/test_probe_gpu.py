@@ -1,4 +1,5 @@
-"""The measured-ceiling probe runs and reports the work it does."""
+"""The measured-ceiling probe runs and reports the work it does; the
+runtime's view of every built kernel matches the planner's LDS arithmetic."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -18,3 +19,28 @@ def test_mfma_probe_runs_and_counts():
         assert t.tdg_mfma_probe_ops(code, 8) == 2 * 32 * 32 * k * 8 * 8 * 2048
     with pytest.raises(t.TdgError):
         t.tdg_mfma_probe(t.TDG_DTYPE_F16F32, 6)   # not a multiple of 4
+
+
+def test_config_resources_match_the_lds_budget():
+    """Every built configuration: the runtime's static LDS equals the
+    planner's lds_stages x (BM*BK + BK*BN) x sizeof(T); the workgroup holds
+    waves x 64 threads; no kernel spills registers; the runtime's
+    workgroups per CU never exceed what 160 KiB of LDS allows."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import tiled_dense_gemm_loop_amd as t
+    t.load_library()
+    for code in (t.TDG_DTYPE_F16F32, t.TDG_DTYPE_I8I32, t.TDG_DTYPE_F32F32):
+        for i in range(t.tdg_config_count(code)):
+            c = t.tdg_config_at(code, i)
+            r = t.tdg_config_resources(code, i)
+            fig = t.tdg_tile_figures(code, c["bm"], c["bn"], c["bk"], c["waves"], c["lds_stages"],
+                                     c["variant"])
+            assert r["lds_bytes"] == fig["lds_bytes"], (code, c, r)
+            assert r["threads"] == 64 * c["waves"], (code, c, r)
+            assert r["spill_bytes"] == 0, (code, c, r)
+            assert 0 < r["vgprs"] <= 512, (code, c, r)
+            assert 1 <= r["wg_per_cu"] <= max(1, 160 * 1024 // r["lds_bytes"]), (code, c, r)
+    with pytest.raises(t.TdgError):
+        t.tdg_config_resources(t.TDG_DTYPE_F16F32, t.tdg_config_count(t.TDG_DTYPE_F16F32))

@@ -49,7 +49,16 @@ EXPORTED = (
     "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
     "gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk", "tdg_splitk_plan",
+    "tdg_config_resources",
 )
+
+
+class TdgKernelResources(ctypes.Structure):
+    _fields_ = [("vgprs", ctypes.c_int), ("spill_bytes", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("threads", ctypes.c_int), ("wg_per_cu", ctypes.c_int)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class TdgConfig(ctypes.Structure):
@@ -119,6 +128,8 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_config_count.restype = c_int
     lib.tdg_config_at.argtypes = [c_int, c_int, ctypes.POINTER(TdgConfig)]
     lib.tdg_config_at.restype = c_int
+    lib.tdg_config_resources.argtypes = [c_int, c_int, ctypes.POINTER(TdgKernelResources)]
+    lib.tdg_config_resources.restype = c_int
     lib.tdg_status_string.argtypes = [c_int]
     lib.tdg_status_string.restype = ctypes.c_char_p
     lib.tdg_set_debug_flags.argtypes = [c_int]
@@ -357,6 +368,16 @@ def tdg_config_at(dtype: int, index: int) -> dict:
     if rc != TDG_OK:
         raise TdgError(rc, "tdg_config_at")
     return c.as_dict()
+
+
+def tdg_config_resources(dtype: int, index: int) -> dict:
+    """Registers, spill bytes, LDS bytes, threads and runtime workgroups per
+    CU of the index-th built configuration's kernel (needs the GPU)."""
+    r = TdgKernelResources()
+    rc = load_library().tdg_config_resources(dtype, index, ctypes.byref(r))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_config_resources")
+    return r.as_dict()
 
 
 def tdg_status_string(status: int) -> str:

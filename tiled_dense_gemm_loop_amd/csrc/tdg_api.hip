@@ -887,6 +887,31 @@ int gemm_f32f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t 
                       stream);
 }
 
+int tdg_config_resources(int dtype, int index, tdg_kernel_resources *out) {
+    if (!out || index < 0 || !dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
+    int count = 0, n = 0;
+    const KernelEntry *table = tdg::kernel_table(&count);
+    const KernelEntry *e = nullptr;
+    for (int i = 0; i < count && !e; i++) {
+        if (table[i].dtype != dtype || table[i].guard) continue;
+        if (n++ == index) e = &table[i];
+    }
+    if (!e) return TDG_ERR_INVALID_ARG;
+    const int rc = device_check();
+    if (rc != TDG_OK) return rc;
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, e->fn) != hipSuccess) return TDG_ERR_LAUNCH;
+    int resident = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident, e->fn, e->threads, 0) != hipSuccess)
+        return TDG_ERR_LAUNCH;
+    out->vgprs = attr.numRegs;
+    out->spill_bytes = (int)attr.localSizeBytes;
+    out->lds_bytes = (int)attr.sharedSizeBytes;
+    out->threads = e->threads;
+    out->wg_per_cu = resident;
+    return TDG_OK;
+}
+
 int tdg_set_debug_flags(int flags) {
     if (flags & ~(TDG_DEBUG_POISON_LDS | TDG_DEBUG_NO_K_ROTATION)) return TDG_ERR_INVALID_ARG;
     return tdg::debug_flags.exchange(flags);
