@@ -110,4 +110,9 @@ WORKLOADS = {
     "fp16_ragged": _wl(6, "fp16_ragged", "f16", 4000, 4000, 4000, "normal"),
     # the pages' third data type (FP32 in, FP32 accumulate) at the headline shape
     "fp32_4096": _wl(7, "fp32_4096", "f32", 4096, 4096, 4096, "normal"),
+    # one GPU's share when the 4096^3 products are split by C row panels over
+    # 8 GPUs: the same seeds, so A is exactly the first 512 rows of the full
+    # workload's A (the generator fills row-major) and B is all of it
+    "fp16_shard8": _wl(4, "fp16_shard8", "f16", 512, 4096, 4096, "normal"),
+    "int8_shard8": _wl(3, "int8_shard8", "i8", 512, 4096, 4096, "uniform_i8"),
 }

@@ -719,7 +719,8 @@ def test_binding_rejects_host_tensors(lib):
 
 # --- the full-size workloads, in the configuration the benchmark times ---------------------
 
-@pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny", "fp32_4096"])
+@pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny", "fp32_4096", "fp16_shard8",
+                                  "int8_shard8"])
 def test_full_size_sampled(lib, name):
     import torch
     wl = si.WORKLOADS[name]
@@ -852,3 +853,19 @@ def test_tall_grid(lib):
     rows, cols = sample_indices(M, N, 4000, seed=88, tile_m=64, tile_n=64)
     check_sampled(C, F16, A, B, rows, cols)
     assert torch.equal(C, gemm(lib, F16, "single", dA, dB))
+
+
+def test_row_panel_shard_is_the_full_products_rows(lib):
+    """Split by C row panels, GPU 0's share (512 x 4096 x 4096) needs no
+    exchange: its INT8 product equals rows 0..511 of the full 4096^3 product
+    bit for bit, whatever tile each size is planned with."""
+    import torch
+    full, shard = si.WORKLOADS["int8_4096"], si.WORKLOADS["int8_shard8"]
+    A, B = full.operands()
+    As, Bs = shard.operands()
+    assert np.array_equal(As, A[:512]) and np.array_equal(Bs, B)
+    dA, dB = to_device(A), to_device(B)
+    C_full = gemm(lib, I8, "pipelined", dA, dB)
+    C_shard = gemm(lib, I8, "pipelined", to_device(As), dB)
+    torch.cuda.synchronize()
+    assert torch.equal(C_shard, C_full[:512])
