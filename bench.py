@@ -70,10 +70,13 @@ def profiled_traffic(kernel_desc: str):
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    # A launch is ~0.1 ms: 400 timed launches (~50 ms) average over the power
-    # controller's settling transient of the first few milliseconds under load.
+    # A launch is ~0.1 ms.  The clocks ramp up over the first tens of
+    # milliseconds under load (FP16 4096^3 on one box: 126 us per launch over
+    # the first 50 launches after 50 warm-ups, a steady 110.8 us after about
+    # 350), so 400 untimed launches come first and the next 400 (~45 ms) are
+    # timed at the steady state.
     p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--workload", default="fp16_4096", choices=sorted(si.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-table", action="store_true", help="skip the per-workload variant table")
