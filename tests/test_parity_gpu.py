@@ -869,3 +869,24 @@ def test_row_panel_shard_is_the_full_products_rows(lib):
     C_shard = gemm(lib, I8, "pipelined", to_device(As), dB)
     torch.cuda.synchronize()
     assert torch.equal(C_shard, C_full[:512])
+
+
+def test_binding_launches_on_the_current_stream(lib):
+    """The binding passes torch's current stream: the raw handle it reads
+    equals torch.cuda.current_stream().cuda_stream, also inside a side
+    stream's context, and a product enqueued there is complete after that
+    stream alone is synchronised."""
+    import torch
+    from tiled_dense_gemm_loop_amd import _binding as b
+    dev = torch.cuda.current_device()
+    assert b._stream_handle(dev) == torch.cuda.current_stream().cuda_stream
+    A8, B8 = si.i8_uniform(256, 256, 61), si.i8_uniform(256, 256, 62)
+    dA, dB = to_device(A8), to_device(B8)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert b._stream_handle(dev) == side.cuda_stream
+        assert b._stream_handle(dev) != torch.cuda.default_stream().cuda_stream
+        C = lib.gemm_i8i32_pipelined(dA, dB)
+    side.synchronize()
+    assert np.array_equal(C.cpu().numpy().astype(np.int64), oracle.gemm_i8(A8, B8))

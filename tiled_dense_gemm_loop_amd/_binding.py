@@ -188,19 +188,39 @@ def _torch():
     return torch
 
 
+_raw_stream_fn = None
+
+
+def _stream_handle(device_index: int) -> int:
+    """The hipStream_t of torch's current stream on a device.  torch's raw
+    query returns the handle directly (~0.1 us); the public
+    torch.cuda.current_stream(...).cuda_stream builds a Stream object first
+    (~2.7 us per call, most of a small GEMM's host cost), so it is only the
+    fallback."""
+    global _raw_stream_fn
+    torch = _torch()
+    if _raw_stream_fn is None:
+        fn = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream_fn = fn if fn is not None else (
+            lambda dev: torch.cuda.current_stream(dev).cuda_stream)
+    return _raw_stream_fn(device_index)
+
+
 def _matrix(t, dtypes, what):
-    if t.dim() != 2:
-        raise ValueError("%s must be 2-D, got shape %s" % (what, tuple(t.shape)))
+    shape = t.shape
+    if len(shape) != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (what, tuple(shape)))
     if t.dtype not in dtypes:
         raise TypeError("%s has dtype %s; expected one of %s" % (what, t.dtype, dtypes))
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % what)
-    rows, cols = t.shape
-    if t.numel() == 0:
+    rows, cols = shape
+    if rows == 0 or cols == 0:
         return rows, cols, t.data_ptr(), max(cols, 1)
-    if cols > 1 and t.stride(1) != 1:
+    st = t.stride()
+    if cols > 1 and st[1] != 1:
         raise ValueError("%s: elements within a row must be contiguous" % what)
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    ld = st[0] if rows > 1 else cols
     return rows, cols, t.data_ptr(), max(ld, 1)
 
 
@@ -240,13 +260,12 @@ def _gemm(name, A, B, C, cfg, f16, splitk=None):
         mid = (parts, ws.data_ptr() if ws is not None else None,
                ws.numel() * ws.element_size() if ws is not None else 0)
     dev = A.device.index
-    if dev is None or dev == torch.cuda.current_device():
-        stream = torch.cuda.current_stream().cuda_stream
-        rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, *mid, stream, *tail)
+    cur = torch.cuda.current_device()
+    if dev is None or dev == cur:
+        rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, *mid, _stream_handle(cur), *tail)
     else:
         with torch.cuda.device(A.device):
-            stream = torch.cuda.current_stream(A.device).cuda_stream
-            rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, *mid, stream, *tail)
+            rc = fn(M, N, K, pa, lda, pb, ldb, pc, ldc, *mid, _stream_handle(dev), *tail)
     if rc != TDG_OK:
         raise TdgError(rc, name)
     return C
