@@ -35,10 +35,14 @@
  *   a pointer may be NULL only when its matrix is empty;
  *   rows * ld * sizeof(element) of each matrix must fit in int64;
  *   the bytes C spans may not overlap those of A or B.
- * Leading dimensions must also satisfy 64 * ld * sizeof(T) + 256 < 2^31 for
- * A and B (the kernels address 64 rows with 32-bit per-lane offsets): about
- * 16 million FP16, 32 million INT8 or 8 million FP32 elements.  Larger ones
- * return TDG_ERR_UNSUPPORTED.
+ * The kernels reach the rows of A and B that one thread loads from with an
+ * unsigned 32-bit per-lane byte offset: for the kernel a call runs,
+ * (R - 1) * ld * sizeof(T) + (row bytes of one tile) must stay below 2^32,
+ * where R is the number of A (or B) tile rows the workgroup's threads cover
+ * with their first chunk (at most 128).  Every built kernel accepts
+ * lda * sizeof(T) and ldb * sizeof(T) up to 33,818,639 bytes (about 16.9
+ * million FP16, 33.8 million INT8 or 8.4 million FP32 elements); a call whose
+ * kernel cannot reach its rows returns TDG_ERR_UNSUPPORTED.
  * Degenerate shapes: M == 0 or N == 0 returns TDG_OK and launches nothing;
  * K == 0 writes zeros to C.
  * Any shape and alignment is accepted.  The fast path needs 16-byte aligned

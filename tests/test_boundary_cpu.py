@@ -10,6 +10,7 @@ import re
 import pytest
 
 import tiled_dense_gemm_loop_amd as tdg
+from conftest import no_device_only
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_worked_examples.json")))
@@ -130,12 +131,56 @@ def test_mfma_probe_arguments():
     assert tdg.tdg_mfma_probe_sink_floats() == 512 * 256
 
 
+def _offset_bounds(dtype, cfg):
+    """Largest lda and ldb (elements) whose rows a kernel reaches with its
+    unsigned 32-bit per-lane offsets: a thread's first chunk lies up to
+    R - 1 rows below the tile's first row, R = threads / (16-byte chunks per
+    image row), and adds up to one image row of bytes."""
+    es = {0: 2, 1: 1, 2: 4}[dtype]
+    threads = cfg["waves"] * 64
+    a_cpr, b_cpr = cfg["bk"] * es // 16, cfg["bn"] * es // 16
+    a_rows, b_rows = threads // a_cpr, threads // b_cpr
+    lim = (1 << 32) - 1
+    lda = (lim - cfg["bk"] * es) // (a_rows - 1) // es
+    ldb = (lim - cfg["bn"] * es) // (b_rows - 1) // es
+    return lda, ldb
+
+
+@no_device_only
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_leading_dimension_bound_of_every_kernel(dtype):
+    """For every built configuration, the largest leading dimensions its
+    32-bit per-lane offsets reach are accepted (the call gets as far as the
+    device check: TDG_ERR_NO_DEVICE on this host) and one element more is
+    refused with TDG_ERR_UNSUPPORTED, for A and for B separately; no call
+    launches anything here.  Every kernel accepts 33,818,639 bytes."""
+    name = {0: "gemm_f16f32_ex", 1: "gemm_i8i32_ex", 2: "gemm_f32f32_ex"}[dtype]
+    es = {0: 2, 1: 1, 2: 4}[dtype]
+    A, B, C = 1 << 40, 1 << 44, 1 << 46
+    for i in range(tdg.tdg_config_count(dtype)):
+        c = tdg.tdg_config_at(dtype, i)
+        cfg = tdg.TdgConfig(**c)
+        M, N, K = c["bm"], c["bn"], 2 * c["bk"]
+        lda, ldb = _offset_bounds(dtype, c)
+        assert min(lda, ldb) * es >= 33818639 - es
+        ok = tdg.call_raw(name, M, N, K, A, lda, B, ldb, C, N, 0, cfg)
+        assert ok == tdg.TDG_ERR_NO_DEVICE, (c, lda, ldb, ok)
+        assert tdg.call_raw(name, M, N, K, A, lda + 1, B, ldb, C, N, 0, cfg) == \
+            tdg.TDG_ERR_UNSUPPORTED, (c, "lda")
+        assert tdg.call_raw(name, M, N, K, A, lda, B, ldb + 1, C, N, 0, cfg) == \
+            tdg.TDG_ERR_UNSUPPORTED, (c, "ldb")
+
+
+@no_device_only
 def test_oversized_leading_dimension_is_unsupported():
-    # 64 rows x lda x 2 bytes must stay below 2^31: lda = 2^24 is just over
-    lda = 1 << 24
+    # the 64 x 64 tile's 256 threads cover 32 rows of A (K tile of 128
+    # bytes): 31 * lda * 2 + 128 bytes must stay below 2^32
+    lda = ((1 << 32) - 1 - 128) // 31 // 2 + 1
     assert tdg.call_raw("gemm_f16f32_pipelined", 64, 64, 64, 1 << 30, lda, 1 << 40, 64,
                         1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
-    assert tdg.call_raw("gemm_i8i32", 64, 64, 64, 1 << 30, 64, 1 << 40, 1 << 25,
+    assert tdg.call_raw("gemm_f16f32_pipelined", 64, 64, 64, 1 << 30, lda - 1, 1 << 40, 64,
+                        1 << 44, 64) == tdg.TDG_ERR_NO_DEVICE
+    assert tdg.call_raw("gemm_i8i32", 64, 64, 64, 1 << 30, 64, 1 << 40, 1 << 27,
                         1 << 44, 64) == tdg.TDG_ERR_UNSUPPORTED
     # a single row may have any leading dimension; one whose 64-row offset
     # would wrap a 64-bit product must still be refused, not launched
@@ -287,6 +332,7 @@ def test_debug_flags_round_trip():
     assert tdg.tdg_set_debug_flags(0) == 0
 
 
+@no_device_only
 def test_concurrent_calls_resolve_consistently():
     """Eight host threads resolve a churn of shapes and explicit configs at
     once through the GEMM entry points (the plan cache holds 16 entries, so
@@ -381,6 +427,7 @@ def test_planner_respects_partial_requests():
     assert cfg["bk"] == 32 and cfg["bm"] == 256
 
 
+@no_device_only
 def test_splitk_plan_and_workspace_validation():
     """Split K is planned only where tiles leave the chip idle, and its
     workspace is checked before any HIP call: missing, short, misaligned or

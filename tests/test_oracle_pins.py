@@ -278,6 +278,40 @@ def test_elementwise_form_matches_full_product():
     assert np.array_equal(c, C[rows, cols]) and np.array_equal(s, S[rows, cols])
 
 
+def test_elementwise_form_on_strided_views():
+    """The single-element forms read A and B through their leading
+    dimensions: on views into wider matrices whose padding holds other
+    values, every requested element equals numpy's product of the views
+    (int64 exactly; float64 within rounding of the summation order) and the
+    full routine's element bit for bit.  Taking N for ldb or K for lda would
+    read the padding and fail."""
+    rng = np.random.default_rng(31)
+    M, N, K = 37, 29, 53
+    Aw = si.i8_uniform(M, K + 11, seed=32)
+    Bw = si.i8_uniform(K, N + 7, seed=33)
+    A, B = Aw[:, 3:3 + K], Bw[:, 5:5 + N]
+    assert A.strides[0] == K + 11 and B.strides[0] == N + 7
+    rows = rng.integers(0, M, 200)
+    cols = rng.integers(0, N, 200)
+    ref = (A.astype(np.int64) @ B.astype(np.int64))[rows, cols]
+    assert np.array_equal(oracle.gemm_i8_at(A, B, rows, cols), ref)
+    assert np.array_equal(oracle.gemm_i8(A, B)[rows, cols], ref)
+    for wide, widen, full, at in (
+            (lambda r, c, s: si.f16_normal(r, c, s), lambda x: x.view(np.float16).astype(np.float64),
+             oracle.gemm_f16, oracle.gemm_f16_at),
+            (lambda r, c, s: si.f32_normal(r, c, s), lambda x: x.astype(np.float64),
+             oracle.gemm_f32, oracle.gemm_f32_at)):
+        Aw, Bw = wide(M, K + 11, 34), wide(K, N + 7, 35)
+        A, B = Aw[:, 3:3 + K], Bw[:, 5:5 + N]
+        c, s = at(A, B, rows, cols)
+        C, S = full(A, B)
+        assert np.array_equal(c, C[rows, cols]) and np.array_equal(s, S[rows, cols])
+        ref = (widen(A) @ widen(B))[rows, cols]
+        ref_s = (np.abs(widen(A)) @ np.abs(widen(B)))[rows, cols]
+        assert np.all(np.abs(c - ref) <= 1e-12 * ref_s)
+        assert np.allclose(s, ref_s, rtol=1e-12, atol=0.0)
+
+
 def test_elementwise_form_rank1_closed_form_at_full_size():
     # 4096-long sums at the largest magnitudes int8 allows
     K = 4096

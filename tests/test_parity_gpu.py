@@ -402,34 +402,43 @@ def test_extreme_aspect_ratios(lib, dtype, M, N, K):
         _check(dtype, gemm(lib, dtype, kind, dA, dB), A, B)
 
 
-@pytest.mark.parametrize("dtype", [F16, I8])
-def test_largest_leading_dimensions(lib, dtype):
-    """The largest 16-byte aligned leading dimensions the per-lane 32-bit
-    offsets accept (64 * ld * sizeof(T) + 256 < 2^31) on the unguarded
-    direct-to-LDS path: whole 128 x 128 x 128 tiles inside matrices whose
-    rows are 32 MiB apart (A and B ~4.3 GB each, C ~8.6 GB)."""
+@pytest.mark.parametrize("dtype,bm,bn,bk,waves", [(F16, 128, 128, 64, 4), (F16, 256, 256, 32, 8),
+                                                  (I8, 128, 128, 128, 4), (I8, 256, 256, 64, 8)])
+def test_largest_leading_dimensions(lib, dtype, bm, bn, bk, waves):
+    """The largest 16-byte aligned leading dimensions a kernel's unsigned
+    32-bit per-lane offsets reach ((R - 1) * ld * sizeof(T) + row bytes
+    < 2^32, R = rows its threads cover with their first chunk: 128 for the
+    8-wave 256 x 256 tiles with a 64-byte K tile), for A and B at once, on
+    whole tiles of the unguarded path, two K tiles, in every loop form.  A
+    and B are views into matrices of 8.7 to 18 GB."""
     import torch
     es = 2 if dtype == F16 else 1
-    ld = ((1 << 31) - 257) // (64 * es)
-    ld -= ld % (16 // es)                     # keep rows 16-byte aligned
-    assert 64 * ld * es + 256 < (1 << 31)
-    M = N = K = 128
+    threads = waves * 64
+    a_rows, b_rows = threads // (bk * es // 16), threads // (bn * es // 16)
+    lim = (1 << 32) - 1
+    lda = (lim - bk * es) // (a_rows - 1) // es
+    ldb = (lim - bn * es) // (b_rows - 1) // es
+    lda -= lda % (16 // es)                   # keep rows 16-byte aligned
+    ldb -= ldb % (16 // es)
+    assert (a_rows - 1) * lda * es + bk * es <= lim and (b_rows - 1) * ldb * es + bn * es <= lim
+    M, N, K = bm, bn, 2 * bk
     A, B = _operands(dtype, M, N, K, seed=77)
     tdt = torch.float16 if dtype == F16 else torch.int8
-    bigA = torch.empty((M, ld), dtype=tdt, device="cuda")
-    bigB = torch.empty((K, ld), dtype=tdt, device="cuda")
-    bigC = torch.empty((M, ld), dtype=torch.float32 if dtype == F16 else torch.int32, device="cuda")
+    bigA = torch.empty((M, lda), dtype=tdt, device="cuda")
+    bigB = torch.empty((K, ldb), dtype=tdt, device="cuda")
     try:
         bigA[:, :K] = to_device(A)
         bigB[:, :N] = to_device(B)
-        C = bigC[:, :N]
-        cfg, info = lib.tdg_plan(CODE[dtype], M, N, K)
-        assert info["guarded"] == 0
-        for kind in ("single", "pipelined"):
-            gemm(lib, dtype, kind, bigA[:, :K], bigB[:, :N], C)
+        outs = []
+        for variant, stages in ((lib.TDG_VARIANT_SINGLE, 1), (lib.TDG_VARIANT_REG_PREFETCH, 2),
+                                (lib.TDG_VARIANT_DIRECT_LDS, 2)):
+            cfg = dict(bm=bm, bn=bn, bk=bk, waves=waves, lds_stages=stages, variant=variant)
+            C = gemm(lib, dtype, "ex", bigA[:, :K], bigB[:, :N], cfg=cfg)
             _check(dtype, C, A, B)
+            outs.append(C)
+        assert all(torch.equal(outs[0], c) for c in outs[1:])
     finally:
-        del bigA, bigB, bigC
+        del bigA, bigB
         torch.cuda.empty_cache()
 
 
@@ -636,14 +645,16 @@ def test_k_rotation_against_the_plain_walk(lib, dtype, M, N, K):
 
 
 @pytest.mark.parametrize("dtype", [F16, I8, F32])
-@pytest.mark.parametrize("M,N,K,parts", [(256, 256, 8192, 0), (256, 256, 8192, 7), (130, 70, 3000, 5),
+@pytest.mark.parametrize("M,N,K,parts", [(256, 256, 8192, 0), (256, 256, 8192, 1), (256, 256, 8192, 7),
+                                         (130, 70, 3000, 5),
                                          (300, 290, 4099, 3), (64, 64, 65536, 0), (512, 384, 2048, 2),
                                          (100, 100, 600, 64)])
 def test_split_k(lib, dtype, M, N, K, parts):
-    """K split over `parts` workgroups per tile (0: the planner's choice; a
-    count above the K tiles is lowered), partial tiles summed in part order:
-    against the oracle, bitwise repeatable, INT8 equal to the unsplit call;
-    once more under the LDS poisoning race screen."""
+    """K split over `parts` workgroups per tile (0: the planner's choice; 1:
+    the plain product, equal to the pipelined call bit for bit; a count above
+    the K tiles is lowered), partial tiles summed in part order: against the
+    oracle, bitwise repeatable, INT8 equal to the unsplit call; once more
+    under the LDS poisoning race screen."""
     import torch
     A, B = _operands(dtype, M, N, K, seed=M + 5 * K + parts)
     dA, dB = to_device(A), to_device(B)
@@ -651,7 +662,7 @@ def test_split_k(lib, dtype, M, N, K, parts):
     C1 = fn(dA, dB, parts=parts)
     _check(dtype, C1, A, B)
     assert torch.equal(C1, fn(dA, dB, parts=parts))
-    if dtype == I8:
+    if dtype == I8 or parts == 1:
         assert torch.equal(C1, gemm(lib, dtype, "pipelined", dA, dB))
     prev = lib.tdg_set_debug_flags(lib.TDG_DEBUG_POISON_LDS)
     try:
@@ -711,17 +722,26 @@ def test_binding_rejects_host_tensors(lib):
     ws = torch.empty(4 * 64 * 64 * 4, dtype=torch.uint8, device="cuda")[::2]  # not contiguous
     with pytest.raises(ValueError):
         lib.gemm_f16f32_splitk(A, B, parts=2, workspace=ws)
+    with pytest.raises(ValueError):  # the C ABI answers TDG_ERR_INVALID_ARG; the binding says so first
+        lib.gemm_f16f32_splitk(A, B, parts=-1)
     x = torch.ones((64, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         lib.tdg_transpose_f32(x, out=torch.empty((64, 64)))
     torch.cuda.synchronize()
 
 
-# --- the full-size workloads, in the configuration the benchmark times ---------------------
+# --- the full-size workloads, in the configuration the benchmark times: whole outputs ------
 
 @pytest.mark.parametrize("name", ["int8_4096", "fp16_4096", "fp16_skinny", "fp32_4096", "fp16_shard8",
                                   "int8_shard8"])
-def test_full_size_sampled(lib, name):
+def test_full_size_whole_output(lib, name):
+    """The benchmark's workloads in the configuration it times: every element
+    of C against the oracle (INT8 bit for bit, FP16 / FP32 within
+    1e-4 * sum |a b|), after a quick check of sampled elements (tile corners
+    included) that gives an early, readable failure.  The sequential loop and
+    every other built loop form at the planner's tile must then equal the
+    pipelined output bit for bit ("Pipeline GPU Kernel", Step 5: check a small
+    size, then the target size, against the CPU reference)."""
     import torch
     wl = si.WORKLOADS[name]
     A, B = wl.operands()
@@ -730,8 +750,8 @@ def test_full_size_sampled(lib, name):
     rows, cols = sample_indices(wl.M, wl.N, 3000, seed=wl.seed_a, tile_n=min(256, wl.N))
     C_pipe = gemm(lib, dtype, "pipelined", dA, dB)
     check_sampled(C_pipe, dtype, A, B, rows, cols)
+    _check(dtype, C_pipe, A, B)
     C_single = gemm(lib, dtype, "single", dA, dB)
-    check_sampled(C_single, dtype, A, B, rows, cols)
     assert torch.equal(C_pipe, C_single)
     tile, _ = lib.tdg_plan(CODE[dtype], wl.M, wl.N, wl.K)
     for vname, cfg in _variants(lib, dtype, tile):
@@ -742,11 +762,12 @@ def test_full_size_sampled(lib, name):
 
 @pytest.mark.parametrize("dtype,M,N,K", [(F16, 4095, 4095, 4095), (I8, 4097, 4097, 4097),
                                          (F32, 4095, 4095, 4095)])
-def test_large_odd_sampled(lib, dtype, M, N, K):
+def test_large_odd_whole_output(lib, dtype, M, N, K):
     """Odd sizes near the benchmark sizes: most rows start off a 16-byte
-    boundary, so the planner takes the guarded register-prefetch loop;
-    sampled elements (tile edges included) against the oracle, and the whole
-    output against the guarded sequential loop."""
+    boundary, so the planner takes the guarded register-prefetch loop; every
+    element against the oracle (sampled tile edges first, for an early
+    failure message), and the whole output against the guarded sequential
+    loop bit for bit."""
     import torch
     A, B = _operands(dtype, M, N, K, seed=M + 7)
     dA, dB = to_device(A), to_device(B)
@@ -756,6 +777,7 @@ def test_large_odd_sampled(lib, dtype, M, N, K):
     rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=cfg["bn"])
     C = gemm(lib, dtype, "pipelined", dA, dB)
     check_sampled(C, dtype, A, B, rows, cols)
+    _check(dtype, C, A, B)
     single = dict(cfg, variant=lib.TDG_VARIANT_SINGLE, lds_stages=1)
     assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=single))
     del C, dA, dB
@@ -764,10 +786,11 @@ def test_large_odd_sampled(lib, dtype, M, N, K):
 
 @pytest.mark.parametrize("dtype,M,N,K", [(F16, 4000, 4000, 4000), (I8, 4000, 4000, 4000),
                                          (F16, 16383, 64, 8184), (F32, 4000, 4000, 4000)])
-def test_large_ragged_sampled(lib, dtype, M, N, K):
+def test_large_ragged_whole_output(lib, dtype, M, N, K):
     """Ragged shapes near the benchmark sizes run the bounds-checked
-    direct-to-LDS loop; sampled elements (tile edges included) against the
-    oracle, and the whole output against the element-wise guarded loop."""
+    direct-to-LDS loop; every element against the oracle (sampled tile edges
+    first), and the whole output against the guarded register-prefetch loop
+    bit for bit."""
     import torch
     A, B = _operands(dtype, M, N, K, seed=M + K)
     dA, dB = to_device(A), to_device(B)
@@ -777,6 +800,7 @@ def test_large_ragged_sampled(lib, dtype, M, N, K):
     rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=min(cfg["bn"], N))
     C = gemm(lib, dtype, "pipelined", dA, dB)
     check_sampled(C, dtype, A, B, rows, cols)
+    _check(dtype, C, A, B)
     reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
     assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
     del C, dA, dB
@@ -843,8 +867,9 @@ def test_fp16_long_k_exact(lib):
 
 
 def test_tall_grid(lib):
-    """M = 2^20 rows, N = 64: 16384 workgroups; sampled rows against the
-    oracle, the whole output against the sequential loop."""
+    """M = 2^20 rows, N = 64: 16384 workgroups; every element against the
+    oracle (sampled rows first), and the whole output against the sequential
+    loop bit for bit."""
     import torch
     M, N, K = 1 << 20, 64, 128
     A, B = _operands(F16, M, N, K, seed=88)
@@ -852,6 +877,7 @@ def test_tall_grid(lib):
     C = gemm(lib, F16, "pipelined", dA, dB)
     rows, cols = sample_indices(M, N, 4000, seed=88, tile_m=64, tile_n=64)
     check_sampled(C, F16, A, B, rows, cols)
+    check_f16(C, A, B)
     assert torch.equal(C, gemm(lib, F16, "single", dA, dB))
 
 

@@ -250,10 +250,17 @@ def _gemm(name, A, B, C, cfg, f16, splitk=None):
     mid = ()
     if splitk is not None:  # (parts, workspace tensor or None)
         parts, ws = splitk
+        parts = int(parts)
+        if parts < 0:
+            raise ValueError("parts must be >= 0 (0: the planner's choice), got %d" % parts)
         if ws is None:
-            parts, need = (parts, parts * M * N * 4) if parts > 1 else tdg_splitk_plan(
-                {"gemm_f16f32_splitk": TDG_DTYPE_F16F32, "gemm_i8i32_splitk": TDG_DTYPE_I8I32,
-                 "gemm_f32f32_splitk": TDG_DTYPE_F32F32}[name], M, N, K)
+            if parts == 0:  # the planner's choice, planned here to size the workspace
+                parts, need = tdg_splitk_plan(
+                    {"gemm_f16f32_splitk": TDG_DTYPE_F16F32, "gemm_i8i32_splitk": TDG_DTYPE_I8I32,
+                     "gemm_f32f32_splitk": TDG_DTYPE_F32F32}[name], M, N, K)
+            else:
+                need = parts * M * N * 4 if parts > 1 else 0
+            # parts == 1 runs the plain product, which needs no workspace
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=A.device) if parts > 1 else None
         elif not ws.is_cuda or ws.device != A.device or not ws.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on %s" % A.device)

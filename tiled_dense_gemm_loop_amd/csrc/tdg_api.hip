@@ -165,12 +165,26 @@ bool aligned_operands(int dtype, const void *A, int64_t lda, const void *B, int6
            ((ldb * es) % 16 == 0);
 }
 
-// Per-lane 32-bit offsets cover up to 64 rows of A or B plus one row of
-// bytes; the planner refuses leading dimensions that would overflow them.
-bool offsets_fit(int dtype, int64_t lda, int64_t ldb) {
-    const int64_t es = elem_size(dtype);
-    const int64_t max_ld = (((int64_t)1 << 31) - 257) / (64 * es);  // 64 ld es + 256 < 2^31
-    return lda <= max_ld && ldb <= max_ld;
+// Whether the per-lane 32-bit offsets of a kernel reach every chunk it loads
+// from A and B.  A thread's first chunk sits (NT / CPR - 1) rows below the
+// tile's first row at most (NT threads, CPR 16-byte chunks per image row:
+// 127 rows for the 8-wave 256-wide tiles with a 64-byte K tile), and the
+// offset adds at most one row's worth of chunk bytes; the hardware reads the
+// offset as an unsigned 32-bit value added to a 64-bit base.  Later chunks
+// and K tiles move the wave-uniform 64-bit base, not the offset.
+bool offsets_fit(const KernelEntry &e, int64_t lda, int64_t ldb) {
+    const uint64_t es = (uint64_t)elem_size(e.dtype);
+    const uint64_t nt = (uint64_t)cfg_waves(e) * 64u;
+    const uint64_t a_cpr = (uint64_t)e.bkb / 16u, b_cpr = (uint64_t)e.bn * es / 16u;
+    const uint64_t a_rows = nt / a_cpr, b_rows = nt / b_cpr;
+    const uint64_t lim = 0xFFFFFFFFull;
+    auto fits = [&](uint64_t rows, int64_t ld, uint64_t row_bytes) {
+        if (ld < 0) return false;
+        if (rows <= 1) return row_bytes <= lim;
+        const uint64_t ld_bytes = (uint64_t)ld * es;  // extent_ok bounds ld * es
+        return ld_bytes <= (lim - row_bytes) / (rows - 1);
+    };
+    return fits(a_rows, lda, (uint64_t)e.bkb) && fits(b_rows, ldb, (uint64_t)e.bn * es);
 }
 
 // Estimated 32-bit registers per lane: accumulators, register staging of one
@@ -516,7 +530,7 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     }
     if (!e) return TDG_ERR_UNSUPPORTED;
     if (e->lds_bytes > kLdsPerCU) return TDG_ERR_UNSUPPORTED;
-    if (!offsets_fit(dtype, lda, ldb)) return TDG_ERR_UNSUPPORTED;
+    if (!offsets_fit(*e, lda, ldb)) return TDG_ERR_UNSUPPORTED;
 
     if (out) {
         out->entry = e;
@@ -537,12 +551,12 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
 }
 
 // Recent resolutions, so that repeated calls on one shape skip the table
-// scans.  The key holds everything resolve() reads: the request, the shape and
-// the two properties of the operands it looks at (alignment and whether the
-// leading dimensions fit the 32-bit per-lane offsets).
+// scans.  The key holds everything resolve() reads: the request, the shape,
+// the operands' alignment and the leading dimensions (which decide whether
+// the chosen kernel's 32-bit per-lane offsets reach every chunk).
 struct PlanKey {
-    int dtype, variant_req, bm, bn, bk, waves, stages, pipelined_default, vec_ok, fits;
-    int64_t M, N, K;
+    int dtype, variant_req, bm, bn, bk, waves, stages, pipelined_default, vec_ok;
+    int64_t M, N, K, lda, ldb;
     bool operator==(const PlanKey &o) const { return memcmp(this, &o, sizeof(PlanKey)) == 0; }
 };
 struct PlanSlot {
@@ -569,10 +583,11 @@ int resolve_cached(int dtype, int64_t M, int64_t N, int64_t K, const void *A, in
     key.stages = req.lds_stages;
     key.pipelined_default = pipelined_default ? 1 : 0;
     key.vec_ok = aligned_operands(dtype, A, lda, B, ldb) ? 1 : 0;
-    key.fits = offsets_fit(dtype, lda, ldb) ? 1 : 0;
     key.M = M;
     key.N = N;
     key.K = K;
+    key.lda = lda;
+    key.ldb = ldb;
     {
         std::lock_guard<std::mutex> lock(g_plan_mutex);
         for (const PlanSlot &slot : g_plans)
