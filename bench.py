@@ -7,10 +7,14 @@ Timing uses HIP events recorded on the stream the kernels are launched on
 --warmup untimed ones ("Analyze Kernel Bottleneck", Step 1: event timing
 after warm-up, effective GFLOPS = 2*M*N*K / t).
 
-Printed: ONE JSON line with the headline value, a roofline object for the
-kernel, the CPU oracle timed on a bounded sample on this host's cores, and a
-side-by-side table of every workload x loop variant (single-buffer,
-register prefetch, direct-to-LDS).
+Printed on stdout: ONE short JSON line with the headline value, the roofline
+object of its kernel (with the metric's three parts -- FP16 and INT8 4096^3
+against the dense MFMA peak, the skinny FP16 product against HBM -- under
+roofline.parts and metric_parts), and the CPU oracle timed on bounded samples
+on this host's cores, per configuration.  The side-by-side table of every
+workload x loop variant (single-buffer, register prefetch, direct-to-LDS),
+the tile sweep, the cold-cache runs, the copy / transpose ladder and the
+measured ceilings go to stderr, and with --detail-out to a JSON file.
 """
 from __future__ import annotations
 
@@ -80,6 +84,8 @@ def parse():
     p.add_argument("--workload", default="fp16_4096", choices=sorted(si.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-table", action="store_true", help="skip the per-workload variant table")
+    p.add_argument("--no-parts", action="store_true",
+                   help="skip timing the metric's other parts (INT8 4096^3, skinny)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--no-ladder", action="store_true", help="skip the copy/transpose ladder")
@@ -91,6 +97,11 @@ def parse():
                    help="timed launches per configuration in the sweep")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (counter calibration)")
+    p.add_argument("--part-cpu-seconds", type=float, default=2.0,
+                   help="target CPU time of the oracle sample for each other configuration")
+    p.add_argument("--detail-out", default=None,
+                   help="also write the full record (variant table, sweep, ladder, ceilings, "
+                        "cold runs) as JSON to this file; it always goes to stderr")
     return p.parse_args()
 
 
@@ -325,35 +336,64 @@ def tile_sweep(tdg, steps: int, warmup: int):
     return rows
 
 
-def cpu_baseline(wl, A, B, target_s: float):
-    """The oracle as it stands, on a bounded sample: the first R rows of C,
-    R chosen so the run takes about target_s seconds on this host; plus the
-    same oracle on one thread for the FP16 1024^3 workload (a per-core
-    figure)."""
+def oracle_rate(wl, A, B, target_s: float, threads: int):
+    """The oracle as it stands on a bounded sample of one workload: the first
+    R rows of C, R chosen so that the run takes about target_s seconds on
+    this host (all of C when that is quicker).  Returns (ops per second, rows,
+    seconds)."""
     import oracle
-    threads = oracle.host_threads()
     fn = {"f16": oracle.gemm_f16, "i8": oracle.gemm_i8, "f32": oracle.gemm_f32}[wl.dtype]
-    probe_rows = max(threads, 16)
+    probe_rows = min(wl.M, max(threads, 16))
     t0 = time.perf_counter()
     fn(A[:probe_rows], B, threads=threads)
     t_probe = time.perf_counter() - t0
     rows = int(min(wl.M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
-    rows = max(threads, (rows // threads) * threads)
+    if rows < wl.M:
+        rows = max(min(threads, wl.M), (rows // threads) * threads)
     t0 = time.perf_counter()
     fn(A[:rows], B, threads=threads)
     secs = time.perf_counter() - t0
-    tops = 2.0 * rows * wl.N * wl.K / secs / 1e12
+    if rows < wl.M and secs < target_s / 3:  # the small probe overestimated the cost per row
+        rows = int(min(wl.M, rows * target_s / max(secs, 1e-6)))
+        if rows < wl.M:
+            rows = max(threads, (rows // threads) * threads)
+        t0 = time.perf_counter()
+        fn(A[:rows], B, threads=threads)
+        secs = time.perf_counter() - t0
+    return 2.0 * rows * wl.N * wl.K / secs, rows, secs
+
+
+def cpu_baseline(wl, A, B, target_s: float, part_s: float, part_names):
+    """The oracle timed on this host's cores: the headline workload on a
+    sample of about target_s seconds, every other named workload on one of
+    about part_s seconds, and the FP16 1024^3 workload on one thread (a
+    per-core figure)."""
+    import oracle
+    threads = oracle.host_threads()
+    ops, rows, secs = oracle_rate(wl, A, B, target_s, threads)
     unit = UNITS[wl.dtype]
+    per = {}
+    for name in part_names:
+        w = si.WORKLOADS[name]
+        if name == wl.name:
+            r_ops, r_rows, r_secs = ops, rows, secs
+        else:
+            a, b = w.operands()
+            r_ops, r_rows, r_secs = oracle_rate(w, a, b, part_s, threads)
+        per[name] = {"value": round(r_ops / 1e9, 3), "unit": "GOP/s", "cores": threads,
+                     "sample": "rows 0..%d of C (%d x %d x %d, %.2f s)" % (
+                         r_rows - 1, r_rows, w.N, w.K, r_secs)}
     small = si.WORKLOADS["fp16_1024"]
     sa, sb = small.operands()
     t0 = time.perf_counter()
     oracle.gemm_f16(sa, sb, threads=1)
     one = time.perf_counter() - t0
-    return {"value": tops, "unit": unit, "cores": threads, "kind": "oracle",
+    return {"value": ops / 1e12, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": "rows 0..%d of C (%d x %d x %d, %.1f s)" % (rows - 1, rows, wl.N, wl.K, secs),
             "cpu_model": cpu_model(),
             "one_thread_fp16_1024": {"seconds": round(one, 3),
-                                     "tflops": round(2.0 * 1024 ** 3 / one / 1e12, 5)}}
+                                     "tflops": round(2.0 * 1024 ** 3 / one / 1e12, 5)},
+            "per_config": per}
 
 
 def main():
@@ -432,9 +472,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    PART_NAMES = ("fp16_4096", "int8_4096", "fp16_skinny")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, A, B, args.cpu_seconds)
+        cpu = cpu_baseline(wl, A, B, args.cpu_seconds, args.part_cpu_seconds,
+                           ("int8_256", "fp16_1024") + PART_NAMES)
 
     kernel_desc = "%dx%dx%d tile, %d waves, %d LDS stages, %s" % (
         cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
@@ -451,13 +493,14 @@ def main():
         achieved, peak, r_unit = round(gbs, 1), HBM_PEAK_GBS, "GB/s"
         measured = ceilings.get("copy_gbs")
     # The metric has three parts: FP16 and INT8 4096^3 against the dense MFMA
-    # peak, and the skinny product against HBM.  `value` is the first; the
-    # three together, each with its fraction of the data-sheet peak and of
-    # the measured ceiling, go in `metric_parts` (from the pipelined rows).
-    # Each part is timed like the headline (args.steps launches after
-    # args.warmup), past the power controller's first milliseconds.
+    # peak, and the skinny product against HBM.  `value` is the headline
+    # workload's; the three together, each with its fraction of the
+    # data-sheet peak (and of the measured ceiling when one was measured) and
+    # the oracle's rate on the same workload, go in `metric_parts` and in
+    # roofline.parts.  Each part is timed like the headline (args.steps
+    # launches after args.warmup).
     parts = None
-    if not args.no_table:
+    if not args.no_parts:
         def part(name, use_gbs, peak_v, unit_v, ceiling_key):
             w = si.WORKLOADS[name]
             if name == wl.name:
@@ -470,12 +513,24 @@ def main():
             tp, bw = throughput(w, t)
             v = round(bw if use_gbs else tp, 1)
             c = ceilings.get(ceiling_key)
-            return {"value": v, "unit": unit_v, "us": round(t * 1e3, 2), "peak": peak_v,
-                    "frac_of_peak": round(v / peak_v, 4),
-                    "frac_of_measured": round(v / c, 4) if c else None}
+            out = {"value": v, "unit": unit_v, "us": round(t * 1e3, 2), "peak": peak_v,
+                   "frac": round(v / peak_v, 4)}
+            if c:
+                out["frac_of_measured"] = round(v / c, 4)
+            if cpu:
+                out["cpu_oracle_gops"] = cpu["per_config"][name]["value"]
+            return out
         parts = {"fp16_4096": part("fp16_4096", False, PEAK["f16"], "TFLOP/s", "mfma_f16_tflops"),
                  "int8_4096": part("int8_4096", False, PEAK["i8"], "TOP/s", "mfma_i8_tops"),
                  "fp16_skinny": part("fp16_skinny", True, HBM_PEAK_GBS, "GB/s", "copy_gbs")}
+        print("# metric parts %s" % json.dumps(parts), file=sys.stderr, flush=True)
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak,
+                "unit": r_unit, "frac": round(achieved / peak, 4), "traffic": traffic}
+    if measured:
+        roofline["measured_peak"] = measured
+        roofline["frac_of_measured"] = round(achieved / measured, 4)
+    if parts:
+        roofline["parts"] = parts
     # the headline is the roofline's own quantity: operations per second for
     # an MFMA-bound product, bytes per second for an HBM-bound one
     line = {
@@ -495,19 +550,20 @@ def main():
                    "accumulate": "i32" if wl.dtype == "i8" else "f32",
                    "kernel": kernel_desc,
                    "parallelism": "none"},
-        "roofline": {"bound": bound, "achieved": achieved, "peak": peak,
-                     "unit": r_unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "measured_peak": measured,
-                     "frac_of_measured": round(achieved / measured, 4) if measured else None},
+        "roofline": roofline,
         "metric_parts": parts,
-        "measured_ceilings": ceilings,
-        "launches": launches,
-        "cold": cold,
         "cpu_baseline": cpu,
-        "variants": table or None,
-        "transpose_ladder": ladder,
-        "tile_sweep": sweep,
     }
+    # Everything else measured goes to stderr and, when asked, to a file: the
+    # one stdout line stays short enough to be read whole.
+    detail = {"line": line, "measured_ceilings": ceilings, "launches": launches, "cold": cold,
+              "variants": table or None, "transpose_ladder": ladder, "tile_sweep": sweep}
+    if args.detail_out:
+        d = os.path.dirname(os.path.abspath(args.detail_out))
+        os.makedirs(d, exist_ok=True)
+        with open(args.detail_out, "w") as f:
+            json.dump(detail, f, indent=1)
+    print("# launches %s" % json.dumps(launches), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 
