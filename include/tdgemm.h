@@ -76,7 +76,8 @@ typedef enum {
     TDG_ERR_INVALID_ARG = -1,
     TDG_ERR_UNSUPPORTED = -2,
     TDG_ERR_LAUNCH = -3,
-    TDG_ERR_NO_DEVICE = -4
+    TDG_ERR_NO_DEVICE = -4,
+    TDG_ERR_SCRATCH = -5 /* gemm_splitk_noalloc: partials exceed its scratch */
 } tdg_status;
 
 typedef enum {
@@ -206,6 +207,29 @@ int gemm_i8i32_splitk(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t 
 int gemm_f32f32_splitk(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                        const float *B, int64_t ldb, float *C, int64_t ldc, int parts,
                        void *workspace, size_t workspace_bytes, void *stream);
+/* Split K with no allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same product as gemm_f16f32_splitk,
+ * gemm_i8i32_splitk or gemm_f32f32_splitk (dtype = TDG_DTYPE_F16F32,
+ * TDG_DTYPE_I8I32 or TDG_DTYPE_F32F32; A, B, C of that entry point's element
+ * types), with the partial products kept in a device array of
+ * TDG_NOALLOC_SCRATCH_BYTES built into the library instead of a caller's
+ * workspace.  The library allocates nothing for it: each GPU holds its own
+ * copy of the array from the first call on that GPU until the process ends.
+ *   parts == 0  the planner's count among those whose partials fit the
+ *               array (1, the plain product, always fits);
+ *   parts >= 2  parts * M * N * 4 bytes must not exceed
+ *               TDG_NOALLOC_SCRATCH_BYTES, else TDG_ERR_SCRATCH before any
+ *               HIP call;
+ *   parts == 1  the plain pipelined product.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and may return wrong
+ * results; calls on one stream are ordered and safe.  Other errors as for
+ * gemm_*_splitk; an unknown dtype is TDG_ERR_INVALID_ARG. */
+#define TDG_NOALLOC_SCRATCH_BYTES (32u << 20)
+int gemm_splitk_noalloc(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                        const void *B, int64_t ldb, void *C, int64_t ldc, int parts, void *stream);
+
 /* The number of K parts the split-K entry points choose for this product (1
  * when splitting is not predicted to be at least 10% faster) and the
  * workspace they then need (0 for 1 part).  Host-only. */

@@ -18,6 +18,8 @@ TDG_ERR_INVALID_ARG = -1
 TDG_ERR_UNSUPPORTED = -2
 TDG_ERR_LAUNCH = -3
 TDG_ERR_NO_DEVICE = -4
+TDG_ERR_SCRATCH = -5
+TDG_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 TDG_DTYPE_F16F32 = 0
 TDG_DTYPE_I8I32 = 1
@@ -49,7 +51,7 @@ EXPORTED = (
     "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
     "gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk", "tdg_splitk_plan",
-    "tdg_config_resources",
+    "tdg_config_resources", "gemm_splitk_noalloc",
 )
 
 
@@ -138,6 +140,8 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = gemm_args[:9] + [c_int, vp, ctypes.c_size_t, vp]
         fn.restype = c_int
+    lib.gemm_splitk_noalloc.argtypes = [c_int] + gemm_args[:9] + [c_int, vp]
+    lib.gemm_splitk_noalloc.restype = c_int
     lib.tdg_splitk_plan.argtypes = [c_int, i64, i64, i64, ctypes.POINTER(c_int),
                                     ctypes.POINTER(ctypes.c_size_t)]
     lib.tdg_splitk_plan.restype = c_int
@@ -374,6 +378,42 @@ def gemm_i8i32_splitk(A, B, C=None, parts: int = 0, workspace=None):
 def gemm_f32f32_splitk(A, B, C=None, parts: int = 0, workspace=None):
     """C (float32) = A . B (float32) with K split over `parts`."""
     return _gemm("gemm_f32f32_splitk", A, B, C, None, "f32", splitk=(parts, workspace))
+
+
+def gemm_splitk_noalloc(A, B, C=None, parts: int = 0):
+    """C = A . B with K split over `parts` (0: the planner's count among those
+    that fit), the partial products kept in the library's built-in scratch
+    array: the library allocates nothing (C is allocated here when not
+    given).  The dtype follows A and B: float16 -> float32 C, int8 -> int32,
+    float32 -> float32.  Calls that overlap in time on one GPU race on the
+    array; calls on one stream do not."""
+    torch = _torch()
+    dt = {torch.float16: TDG_DTYPE_F16F32, torch.int16: TDG_DTYPE_F16F32,
+          torch.int8: TDG_DTYPE_I8I32, torch.float32: TDG_DTYPE_F32F32}.get(A.dtype)
+    if dt is None:
+        raise TypeError("A has dtype %s; expected float16, int8 or float32" % A.dtype)
+    in_types = {TDG_DTYPE_F16F32: (torch.float16, torch.int16), TDG_DTYPE_I8I32: (torch.int8,),
+                TDG_DTYPE_F32F32: (torch.float32,)}[dt]
+    M, K, pa, lda = _matrix(A, in_types, "A")
+    K2, N, pb, ldb = _matrix(B, in_types, "B")
+    if K != K2:
+        raise ValueError("inner dimensions differ: A is %dx%d, B is %dx%d" % (M, K, K2, N))
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    out_type = torch.int32 if dt == TDG_DTYPE_I8I32 else torch.float32
+    if C is None:
+        C = torch.empty((M, N), dtype=out_type, device=A.device)
+    Mc, Nc, pc, ldc = _matrix(C, (out_type,), "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError("C has shape %s, expected %s" % ((Mc, Nc), (M, N)))
+    if C.device != A.device:
+        raise ValueError("C is on %s, A and B on %s" % (C.device, A.device))
+    with torch.cuda.device(A.device):
+        rc = _fn("gemm_splitk_noalloc")(dt, M, N, K, pa, lda, pb, ldb, pc, ldc, int(parts),
+                                         _stream_handle(A.device.index))
+    if rc != TDG_OK:
+        raise TdgError(rc, "gemm_splitk_noalloc")
+    return C
 
 
 def tdg_set_debug_flags(flags: int) -> int:

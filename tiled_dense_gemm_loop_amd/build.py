@@ -33,6 +33,7 @@ UNITS = [
     ("tdg_move.hip", [], "tdg_move.o"),
     ("tdg_probe.hip", [], "tdg_probe.o"),
     ("tdg_reduce.hip", [], "tdg_reduce.o"),
+    ("tdg_noalloc.hip", [], "tdg_noalloc.o"),
 ]
 
 

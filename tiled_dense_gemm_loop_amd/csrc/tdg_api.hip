@@ -676,8 +676,10 @@ double sum_parts_us(int parts, int64_t M, int64_t N) {
 // Split-K plan: the configuration and number of K parts with the least
 // predicted time, for products whose tiles leave most compute units idle.
 // parts = 1 (no split) unless splitting is predicted at least 10% faster.
-// Each part keeps at least two K tiles, so its loop still pipelines.
-int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, int *parts) {
+// Each part keeps at least two K tiles, so its loop still pipelines.  Part
+// counts whose partial products exceed ws_limit bytes are not considered.
+int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, int *parts,
+                  uint64_t ws_limit = UINT64_MAX) {
     tdg_config req;
     memset(&req, 0, sizeof(req));
     const Choice base = choose_config(dtype, M, N, K, req);
@@ -696,6 +698,7 @@ int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, i
             if (p > 1 && k_tiles < 2 * p) break;
             const int64_t per = ceil_div(k_tiles, p);
             const int64_t used = ceil_div(k_tiles, per);
+            if (used > 1 && (uint64_t)used * (uint64_t)M * (uint64_t)N * 4u > ws_limit) continue;
             double t = predict_us(r, fig.wg_per_cu, fig.grid * used, per * bk);
             if (used > 1) t += sum_parts_us((int)used, M, N);
             if (best_t < 0.0 || t < best_t) {
@@ -731,15 +734,25 @@ int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, i
     return TDG_OK;
 }
 
+}  // namespace
+
+namespace tdg {
+
+int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                  int64_t ldb, const void *C, int64_t ldc) {
+    return validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
+}
+
 int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-               int64_t ldb, void *C, int64_t ldc, int parts, void *ws, size_t ws_bytes, void *stream) {
+               int64_t ldb, void *C, int64_t ldc, int parts, void *ws, size_t ws_bytes, void *stream,
+               uint64_t auto_limit) {
     int rc = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
     if (rc != TDG_OK) return rc;
     if (parts < 0) return TDG_ERR_INVALID_ARG;
     tdg_config cfg;
     memset(&cfg, 0, sizeof(cfg));
     if (parts == 0) {
-        rc = splitk_choose(dtype, M, N, K, &cfg, &parts);
+        rc = splitk_choose(dtype, M, N, K, &cfg, &parts, auto_limit);
         if (rc != TDG_OK) return rc;
     }
     if (parts <= 1 || M == 0 || N == 0 || K == 0)
@@ -757,6 +770,10 @@ int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_
     return run(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, cfg.bm ? &cfg : nullptr, true, parts, ws);
 }
 
+}  // namespace tdg
+
+namespace {
+using tdg::run_splitk;
 }  // namespace
 
 extern "C" {
@@ -939,6 +956,7 @@ const char *tdg_status_string(int status) {
         case TDG_ERR_UNSUPPORTED: return "unsupported configuration";
         case TDG_ERR_LAUNCH: return "kernel launch failed";
         case TDG_ERR_NO_DEVICE: return "no gfx950 device";
+        case TDG_ERR_SCRATCH: return "partial products exceed the built-in scratch array";
         default: return "unknown status";
     }
 }

@@ -1,6 +1,7 @@
 // tdg_internal.h -- declarations shared by the kernel table and the host API.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace tdg {
@@ -33,5 +34,17 @@ int device_check();
 // INT8.  Enqueued on `stream`.
 int launch_sum_parts(int dtype, int parts, const void *ws, int64_t M, int64_t N, void *C, int64_t ldc,
                      void *stream);
+
+// Argument validation of a GEMM call (TDG_OK or TDG_ERR_INVALID_ARG); no
+// HIP call.
+int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                  int64_t ldb, const void *C, int64_t ldc);
+
+// Split K into the workspace ws of ws_bytes bytes (the gemm_*_splitk entry
+// points).  With parts == 0 the planner chooses the count, among the counts
+// whose partial products take at most auto_limit bytes.
+int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+               int64_t ldb, void *C, int64_t ldc, int parts, void *ws, size_t ws_bytes, void *stream,
+               uint64_t auto_limit = UINT64_MAX);
 
 }  // namespace tdg
