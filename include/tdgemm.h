@@ -249,6 +249,18 @@ int tdg_splitk_plan(int dtype, int64_t M, int64_t N, int64_t K, int *parts,
  * arithmetic: needs no device. */
 int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info);
 
+/* The planner's predicted kernel time, in microseconds, of one row of its
+ * measured-time table -- a built direct-to-LDS configuration with a 128-byte
+ * K tile: tile bm x bn, `waves` waves, `stages` LDS buffers -- for an
+ * M x N x K product: full rounds of (256 compute units x workgroups per
+ * unit) workgroups, then the partial round, each priced from times measured
+ * on MI355X against workgroup count and K.  The prediction is positive and
+ * non-decreasing in M, N and K.  TDG_ERR_UNSUPPORTED when the table has no
+ * such row; TDG_ERR_INVALID_ARG for a bad dtype, size or NULL us.
+ * Host-only. */
+int tdg_predict_us(int dtype, int bm, int bn, int waves, int stages, int64_t M, int64_t N, int64_t K,
+                   double *us);
+
 /* The planner's arithmetic for any tile, built or not: the compute/load
  * ratio and its band, the LDS bytes of `stages` buffers ("Pipeline GPU
  * Kernel", Step 1 and Step 2), the workgroups per MI355X compute unit (LDS,

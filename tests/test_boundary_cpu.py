@@ -415,6 +415,55 @@ def test_planner_picks_by_predicted_time():
     assert _plan_str(I8, 2560, 2560, 2560) == "128x128 w4 s2 direct_lds"
 
 
+def _perf_rows(dtype):
+    """(bm, bn, waves, stages) of every row of the measured-time table."""
+    rows = []
+    for i in range(tdg.tdg_config_count(dtype)):
+        c = tdg.tdg_config_at(dtype, i)
+        es = {0: 2, 1: 1, 2: 4}[dtype]
+        if c["variant"] != tdg.TDG_VARIANT_DIRECT_LDS or c["bk"] * es != 128:
+            continue
+        key = (c["bm"], c["bn"], c["waves"], c["lds_stages"])
+        try:
+            tdg.tdg_predict_us(dtype, *key, 256, 256, 256)
+        except tdg.TdgError:
+            continue
+        rows.append(key)
+    return rows
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_time_model_is_positive_and_monotone(dtype):
+    """Over the planner's domain (1 to ~4800 workgroups, K from 16 to 2^20)
+    every row's predicted time is positive, never falls when workgroups are
+    added (more rows of C) or K grows, and a K split into P parts is never
+    predicted faster than one of its parts alone (P times the workgroups on
+    K / P against the workgroups on K / P)."""
+    rows = _perf_rows(dtype)
+    assert len(rows) >= 5
+    Ks = [16, 256, 1000, 1024, 2048, 4096, 6000, 16384, 65536, 1 << 20]
+    for bm, bn, w, st in rows:
+        for n_tiles_n in (1, 3, 8, 16, 48):
+            N = n_tiles_n * bn
+            prev_k = None
+            for K in Ks:
+                prev_m = 0.0
+                for tiles_m in (1, 2, 4, 7, 8, 16, 24, 33, 48, 64, 96, 100):
+                    t = tdg.tdg_predict_us(dtype, bm, bn, w, st, tiles_m * bm, N, K)
+                    assert t > 0.0, (bm, bn, w, st, tiles_m, N, K, t)
+                    assert t >= prev_m - 1e-9, (bm, bn, w, st, tiles_m, N, K, t, prev_m)
+                    prev_m = t
+                t = tdg.tdg_predict_us(dtype, bm, bn, w, st, 16 * bm, N, K)
+                if prev_k is not None:
+                    assert t >= prev_k - 1e-9, (bm, bn, w, st, N, K, t, prev_k)
+                prev_k = t
+            for P in (2, 4, 16, 64):
+                K = 65536
+                part = tdg.tdg_predict_us(dtype, bm, bn, w, st, 2 * bm, N, K // P)
+                split = tdg.tdg_predict_us(dtype, bm, bn, w, st, 2 * bm * P, N, K // P)
+                assert split >= part - 1e-9
+
+
 def test_planner_respects_partial_requests():
     """A request that fixes part of the configuration is completed within it;
     one outside the measured table (a 64-byte K tile) falls back to the tile

@@ -51,7 +51,7 @@ EXPORTED = (
     "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
     "gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk", "tdg_splitk_plan",
-    "tdg_config_resources", "gemm_splitk_noalloc",
+    "tdg_config_resources", "gemm_splitk_noalloc", "tdg_predict_us",
 )
 
 
@@ -140,6 +140,9 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = gemm_args[:9] + [c_int, vp, ctypes.c_size_t, vp]
         fn.restype = c_int
+    lib.tdg_predict_us.argtypes = [c_int, c_int, c_int, c_int, c_int, i64, i64, i64,
+                                   ctypes.POINTER(ctypes.c_double)]
+    lib.tdg_predict_us.restype = c_int
     lib.gemm_splitk_noalloc.argtypes = [c_int] + gemm_args[:9] + [c_int, vp]
     lib.gemm_splitk_noalloc.restype = c_int
     lib.tdg_splitk_plan.argtypes = [c_int, i64, i64, i64, ctypes.POINTER(c_int),
@@ -353,6 +356,17 @@ def tdg_tile_figures(dtype: int, bm: int, bn: int, bk: int, waves: int = 4, stag
     if rc != TDG_OK:
         raise TdgError(rc, "tdg_tile_figures")
     return info.as_dict()
+
+
+def tdg_predict_us(dtype: int, bm: int, bn: int, waves: int, stages: int, M: int, N: int,
+                   K: int) -> float:
+    """The planner's predicted kernel time (us) of one measured configuration
+    for an M x N x K product."""
+    us = ctypes.c_double()
+    rc = load_library().tdg_predict_us(dtype, bm, bn, waves, stages, M, N, K, ctypes.byref(us))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_predict_us")
+    return us.value
 
 
 def tdg_splitk_plan(dtype: int, M: int, N: int, K: int):

@@ -334,20 +334,31 @@ const PerfRow kPerf[] = {
 
 // Interpolated T(x, K) of one row; below the first n the time is flat, and
 // K below 1024 is taken as 1024 (small products sit at the launch floor,
-// where the line through the two measured K says nothing).
+// where the line through the two measured K says nothing).  The measured
+// points are first made non-decreasing in n at this K (a running maximum:
+// more workgroups never finish sooner) and at least kMinUs (no launch is
+// free), so the model is positive and non-decreasing in n and, with every
+// slope b >= 0, in K, whatever the fitted lines do between and beyond the
+// two measured K.
+constexpr double kMinUs = 1.0;
 double perf_at(const PerfRow &r, int64_t x, int64_t K) {
     const double k = (double)(K < 1024 ? 1024 : K);
     constexpr int P = (int)(sizeof(kPerfN) / sizeof(kPerfN[0]));
-    if (x <= kPerfN[0]) return r.a[0] + r.b[0] * k;
+    double t[P];
+    double run = kMinUs;
+    for (int i = 0; i < P; i++) {
+        const double v = (double)r.a[i] + (double)(r.b[i] > 0.0f ? r.b[i] : 0.0f) * k;
+        run = v > run ? v : run;
+        t[i] = run;
+    }
+    if (x <= kPerfN[0]) return t[0];
     for (int i = 1; i < P; i++) {
         if (x <= kPerfN[i]) {
             const double f = (double)(x - kPerfN[i - 1]) / (double)(kPerfN[i] - kPerfN[i - 1]);
-            const double a = r.a[i - 1] + f * (r.a[i] - r.a[i - 1]);
-            const double b = r.b[i - 1] + f * (r.b[i] - r.b[i - 1]);
-            return a + b * k;
+            return t[i - 1] + f * (t[i] - t[i - 1]);
         }
     }
-    return (r.a[P - 1] + r.b[P - 1] * k) * (double)x / (double)kPerfN[P - 1];
+    return t[P - 1] * (double)x / (double)kPerfN[P - 1];
 }
 
 // Predicted kernel time for `tiles` workgroups: full rounds of slots =
@@ -845,6 +856,21 @@ int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_pl
     const void *aligned = (const void *)(uintptr_t)4096;
     const int64_t lda = K > 0 ? K : 1, ldb = N > 0 ? N : 1;
     return resolve(dtype, M, N, K, aligned, lda, aligned, ldb, req, true, nullptr, out, info);
+}
+
+int tdg_predict_us(int dtype, int bm, int bn, int waves, int stages, int64_t M, int64_t N, int64_t K,
+                   double *us) {
+    if (!dtype_ok(dtype) || !dims_ok(M, N, K) || !us) return TDG_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    for (const PerfRow &r : kPerf) {
+        if (r.dtype != dtype || r.bm != bm || r.bn != bn || r.waves != waves || r.stages != stages)
+            continue;
+        tdg_plan_info fig;
+        tile_figures(dtype, r.bm, r.bn, 128 / es, r.waves, r.stages, TDG_VARIANT_DIRECT_LDS, M, N, K, &fig);
+        *us = predict_us(r, fig.wg_per_cu, fig.grid, K);
+        return TDG_OK;
+    }
+    return TDG_ERR_UNSUPPORTED;
 }
 
 int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant,

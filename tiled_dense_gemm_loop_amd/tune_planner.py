@@ -7,10 +7,14 @@ K = 1024 and K = 4096 on one MI355X: n tiles laid out close to square
 (tiles_m x tiles_n from GRIDS), each point timed as HIP-graph replays (FP16,
 INT8) or back-to-back launches (FP32, whose kernels are long enough).  Each
 series is made non-decreasing in n (a later point caps the earlier ones:
-more workgroups cannot finish sooner), and (a, b) follow from the two K.
+more workgroups cannot finish sooner), and (a, b) follow from the two K.  A
+fitted intercept below zero (the K = 1024 time is less than a quarter of the
+K = 4096 one) is clamped to zero, keeping the K = 4096 point: no launch
+costs less than nothing.  Given several measurement files (several boxes),
+emit averages them point by point before fitting.
 
     python -m tiled_dense_gemm_loop_amd.tune_planner measure times.json   # GPU
-    python -m tiled_dense_gemm_loop_amd.tune_planner emit times.json      # C++ rows
+    python -m tiled_dense_gemm_loop_amd.tune_planner emit times.json [more.json ...]
 
 The emitted rows replace kPerf in csrc/tdg_api.hip.
 """
@@ -76,26 +80,41 @@ def measure(path):
     json.dump(out, open(path, "w"))
 
 
-def emit(path):
-    data = json.load(open(path))
-    lo, hi = data[str(KS[0])], data[str(KS[1])]
+def fit_row(t1, t4):
+    """(a, b) of T = a + b * K through the K = 1024 and K = 4096 series,
+    with negative intercepts clamped to zero (the K = 4096 point kept)."""
+    a_out, b_out = [], []
+    for x, y in zip(t1, t4):
+        b = (y - x) / (KS[1] - KS[0])
+        a = x - KS[0] * b
+        if a < 0.0:
+            a, b = 0.0, y / KS[1]
+        a_out.append(a)
+        b_out.append(max(b, 0.0))
+    return a_out, b_out
+
+
+def emit(*paths):
+    datas = [json.load(open(p)) for p in paths]
+
+    def mean_series(k, key):
+        per = [d[str(k)][key] for d in datas if key in d.get(str(k), {})]
+        return [sum(r[i][1] for r in per) / len(per) for i in range(len(per[0]))]
     ns = [tm * tn for tm, tn in GRIDS]
     print("const int kPerfN[%d] = {%s};" % (len(ns), ", ".join(str(n) for n in ns)))
     print("const PerfRow kPerf[] = {")
     for dt, code, _ in DTYPES:
         for bm, bn, w, s in ORDER:
             key = "%s %dx%d w%d s%d" % (dt, bm, bn, w, s)
-            if key not in hi:
+            if not all(key in d.get(str(KS[1]), {}) for d in datas):
                 continue
 
-            def series(d):
-                t = [v for _, v in d[key]]
+            def series(k):
+                t = mean_series(k, key)
                 for i in range(len(t) - 2, -1, -1):   # more workgroups never finish sooner
                     t[i] = min(t[i], t[i + 1])
                 return t
-            t1, t4 = series(lo), series(hi)
-            b = [(y - x) / (KS[1] - KS[0]) for x, y in zip(t1, t4)]
-            a = [x - KS[0] * bb for x, bb in zip(t1, b)]
+            a, b = fit_row(series(KS[0]), series(KS[1]))
             print("    {%d, %d, %d, %d, %d, {%s},\n     {%s}}," % (
                 code, bm, bn, w, s, ", ".join("%.2ff" % v for v in a),
                 ", ".join("%.6ff" % v for v in b)))
@@ -103,4 +122,7 @@ def emit(path):
 
 
 if __name__ == "__main__":
-    {"measure": measure, "emit": emit}[sys.argv[1]](sys.argv[2])
+    if sys.argv[1] == "measure":
+        measure(sys.argv[2])
+    else:
+        emit(*sys.argv[2:])
