@@ -271,6 +271,109 @@ def test_ragged_direct_padded_rows(lib, dtype):
     _check(dtype, C, A, B)
 
 
+# --- K or N that splits a 16-byte chunk, rows still 16-byte aligned --------------------
+# These keep the direct-to-LDS copy: chunks are fetched whole, and the kernel
+# clears A's bytes at k >= K in the one chunk per row that K splits.  The
+# operands are views into wider storage whose padding holds NaN (INT8: 127),
+# so a byte past K or N that reached a stored sum would show.
+
+POISON = {F16: np.uint16(0x7E00), I8: np.int8(127), F32: np.float32("nan")}
+
+
+def _split_chunk_operands(dtype, M, N, K, seed, pad_chunks=1):
+    """(A, B, dA, dB): host operands and device views of them whose rows are
+    16-byte aligned, ld = K (or N) rounded up to whole 16-byte chunks plus
+    pad_chunks more, padding filled with POISON."""
+    es = {F16: 2, I8: 1, F32: 4}[dtype]
+    epc = 16 // es
+    lda = -(-K // epc) * epc + pad_chunks * epc
+    ldb = -(-N // epc) * epc + pad_chunks * epc
+    A, B = _operands(dtype, M, N, K, seed=seed)
+    bigA = np.full((M, lda), POISON[dtype], dtype=A.dtype)
+    bigB = np.full((K, ldb), POISON[dtype], dtype=B.dtype)
+    bigA[:, :K] = A
+    bigB[:, :N] = B
+    return A, B, to_device(bigA)[:, :K], to_device(bigB)[:, :N]
+
+
+SPLIT_CHUNK = [(300, 270, 137), (257, 129, 263), (64, 63, 65), (5, 7, 3), (1000, 61, 1001),
+               (130, 400, 529), (256, 256, 255), (64, 64, 129)]
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+@pytest.mark.parametrize("M,N,K", SPLIT_CHUNK)
+def test_split_chunk_direct_shapes(lib, dtype, M, N, K):
+    """K and / or N ending inside a 16-byte chunk, aligned rows: the planner
+    keeps the bounds-checked direct-to-LDS loop; the result matches the
+    oracle and, bit for bit, the guarded register-prefetch loop (which
+    zeroes the same bytes in registers) and the two-buffer DMA ring."""
+    import torch
+    A, B, dA, dB = _split_chunk_operands(dtype, M, N, K, seed=5 * M + 3 * N + K)
+    code = CODE[dtype]
+    cfg, info = lib.tdg_plan(code, M, N, K)
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    _check(dtype, C, A, B)
+    direct = dict(cfg, variant=lib.TDG_VARIANT_DIRECT_LDS, lds_stages=2)
+    reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
+    Cd = gemm(lib, dtype, "ex", dA, dB, cfg=direct)
+    _check(dtype, Cd, A, B)
+    assert torch.equal(Cd, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
+    if info["num_tiles"] >= 2:
+        assert torch.equal(C, Cd)
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_split_chunk_direct_every_tile_and_ring(lib, dtype):
+    """A long K that ends inside a chunk, N too: every tile and every ring
+    depth built (interior workgroups run the plain DMA, then the checked one
+    from the partial tile on) against the oracle and bit for bit against the
+    tile's sequential loop; once more under the LDS poisoning race screen."""
+    import torch
+    M, N, K = 300, 270, {F16: 2001, I8: 4013, F32: 1001}[dtype]
+    A, B, dA, dB = _split_chunk_operands(dtype, M, N, K, seed=96)
+    for tile in _tiles(CODE[dtype]):
+        ref_out = None
+        for name, cfg in _variants(lib, dtype, tile):
+            C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+            if ref_out is None:
+                _check(dtype, C, A, B)
+                ref_out = C
+            else:
+                assert torch.equal(ref_out, C), "%s differs at tile %s" % (name, tile)
+            if cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS:
+                prev = lib.tdg_set_debug_flags(lib.TDG_DEBUG_POISON_LDS)
+                try:
+                    C2 = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+                finally:
+                    lib.tdg_set_debug_flags(prev)
+                assert torch.equal(ref_out, C2), "%s differs under the LDS poison" % name
+
+
+@pytest.mark.parametrize("dtype", [F16, I8])
+def test_split_chunk_direct_rotated_and_split_k(lib, dtype):
+    """The straddling K tile at every position of a rotated K walk (a skinny
+    product whose B fits in L2), and inside one part of a split-K product."""
+    import torch
+    M, N, K = 4000, 61, 2003
+    A, B, dA, dB = _split_chunk_operands(dtype, M, N, K, seed=95)
+    cfg, info = lib.tdg_plan(CODE[dtype], M, N, K)
+    assert info["k_rotated"] == 1
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    _check(dtype, C, A, B)
+    prev = lib.tdg_set_debug_flags(lib.TDG_DEBUG_NO_K_ROTATION)
+    try:
+        plain = gemm(lib, dtype, "pipelined", dA, dB)
+    finally:
+        lib.tdg_set_debug_flags(prev)
+    _check(dtype, plain, A, B)
+    if dtype == I8:
+        assert torch.equal(C, plain)
+    fn = {F16: lib.gemm_f16f32_splitk, I8: lib.gemm_i8i32_splitk}[dtype]
+    A2, B2, dA2, dB2 = _split_chunk_operands(dtype, 256, 256, 6001, seed=94)
+    C2 = fn(dA2, dB2, parts=5)
+    _check(dtype, C2, A2, B2)
+
+
 @pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_k_zero_writes_zeros(lib, dtype):
     import torch
@@ -780,6 +883,29 @@ def test_large_odd_whole_output(lib, dtype, M, N, K):
     _check(dtype, C, A, B)
     single = dict(cfg, variant=lib.TDG_VARIANT_SINGLE, lds_stages=1)
     assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=single))
+    del C, dA, dB
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_large_split_chunk_whole_output(lib, dtype):
+    """4095^3 stored with leading dimensions 4096 (rows 16-byte aligned, K
+    and N ending inside a chunk, NaN / 127 in the padding column): the
+    planner keeps the bounds-checked direct-to-LDS loop; every element
+    against the oracle and the whole output bit for bit against the guarded
+    register-prefetch loop."""
+    import torch
+    M = N = K = 4095
+    A, B, dA, dB = _split_chunk_operands(dtype, M, N, K, seed=4095 + 11, pad_chunks=0)
+    assert dA.stride(0) == 4096 and dB.stride(0) == 4096
+    code = CODE[dtype]
+    cfg, info = lib.tdg_plan(code, M, N, K)
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=cfg["bn"])
+    check_sampled(C, dtype, A, B, rows, cols)
+    _check(dtype, C, A, B)
+    reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
+    assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
     del C, dA, dB
     torch.cuda.empty_cache()
 

@@ -151,13 +151,12 @@ bool fast_ok(const KernelEntry &e, int64_t M, int64_t N, int64_t K, bool vec_ok)
 }
 
 // Whether the bounds-checked direct-to-LDS loop may run on a ragged shape:
-// every 16-byte chunk of a row is either wholly inside the matrix or wholly
-// outside it (K and N whole chunks, aligned rows), so out-of-range chunks can
-// be fetched from a zero block and no DMA reads past an operand.
-bool edge_ok(const KernelEntry &e, int64_t N, int64_t K, bool vec_ok) {
-    const int epc = 16 / elem_size(e.dtype);
-    return vec_ok && K > 0 && K % epc == 0 && N % epc == 0;
-}
+// with 16-byte aligned operands and rows every 16-byte chunk starts on a
+// 16-byte boundary, so it lies in one page; chunks that start outside an
+// operand are fetched from a zero block, those that start inside are
+// fetched whole (the kernel clears A's bytes at k >= K when K splits a
+// chunk; B's bytes past N feed only C columns that are not stored).
+bool edge_ok(int64_t K, bool vec_ok) { return vec_ok && K > 0; }
 
 bool aligned_operands(int dtype, const void *A, int64_t lda, const void *B, int64_t ldb) {
     const int es = elem_size(dtype);
@@ -486,7 +485,7 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     };
     const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
     const bool fast = fast_ok(*tile, M, N, K, vec_ok);
-    const bool edge = !fast && edge_ok(*tile, N, K, vec_ok);
+    const bool edge = !fast && edge_ok(K, vec_ok);
 
     int variant = req.variant;
     // With one K tile there is nothing to overlap ("Pipeline GPU Kernel",

@@ -504,13 +504,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // inline assembly so that the compiler does not guard the other buffer's
     // LDS reads with a wait on these copies; completion is awaited
     // explicitly (vmcnt) before the barrier that publishes the tile.
-    // Bounds-checked DMA (GUARD, with the `checked` tag set): the operands are
-    // 16-byte aligned with K and N whole 16-byte chunks, so a chunk is either
-    // wholly inside its matrix or wholly outside; one outside (A row >= M,
-    // k >= K; B row k >= K, column >= N) is fetched from the zero block
-    // instead.  The source is then a per-lane 64-bit address.  B columns >= N
-    // and A rows >= M only feed C elements that are never stored; k >= K must
-    // be zero.  A bounds-checked kernel issues the plain form (wave-uniform
+    // Bounds-checked DMA (GUARD, with the `checked` tag set): the operands'
+    // rows are 16-byte aligned, so every 16-byte chunk starts on a 16-byte
+    // boundary.  A chunk that starts outside its matrix (A row >= M, k >= K;
+    // B row k >= K, column >= N) is fetched from the zero block instead; one
+    // that starts inside is fetched whole, also when K or N ends inside it
+    // (it lies in one 4 KiB page with a byte of the matrix).  The source is
+    // then a per-lane 64-bit address.  B columns >= N and A rows >= M only
+    // feed C elements that are never stored; k >= K must be zero, which the
+    // zero block gives for whole chunks and clear_k_tail for the one A chunk
+    // per row that K splits.  A bounds-checked kernel issues the plain form (wave-uniform
     // base, 32-bit lane offset) for every K tile known to lie wholly inside
     // the operands, so only edge workgroups and the K tail pay for checks.
     constexpr int EPC = 16 / G::ES;
@@ -764,12 +767,53 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 if (w >= w_chk) issue_direct(off, w, checked_t{});
                 else issue_direct(off, w, unchecked_t{});
             };
+            // A K that splits a 16-byte chunk (rows still 16-byte aligned):
+            // the last K tile's straddling chunk of every A row is fetched
+            // whole -- a 16-byte aligned chunk lies inside one 4 KiB page,
+            // and its first byte is inside A -- so its bytes at k >= K hold
+            // whatever follows in memory.  Once that tile has landed and
+            // been published, each row's chunk is cleared from byte
+            // (K - k0) * sizeof(T) % 16 on, and a second barrier publishes
+            // the cleared tile before any fragment is read.  (B needs no
+            // such step: B rows k >= K come from the zero block, and B's
+            // bytes past an N that splits a chunk only feed C columns that
+            // are never stored.)
+            int w_part = -1;   // walk position of the tile with the straddling chunk
+            int kr_part = 0;   // valid k of that tile
+            if constexpr (GUARD) {
+                const int last = args.k_tiles - 1;
+                if (((args.K * G::ES) & 15) != 0 && last >= kb && last < kb + nt) {
+                    const int w = last - kb - krot;
+                    w_part = w < 0 ? w + nt : w;
+                    kr_part = args.K - last * G::BK;
+                }
+            }
+            auto clear_k_tail = [&](int w) __attribute__((always_inline)) {
+                if (!GUARD || w != w_part) return;
+                if (tid < BM) {
+                    const int lc = (kr_part * G::ES) >> 4;          // the straddling chunk
+                    const uint32_t keep = (uint32_t)((kr_part * G::ES) & 15);  // its valid bytes
+                    unsigned char *p = smem + (w % STAGES) * G::STAGE_BYTES + tid * G::BKB +
+                                       ((lc ^ G::swz_a(tid)) << 4);
+                    const u32x4 v = lds_read16(p);
+                    uint32_t w4[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int left = (int)keep - 4 * j;
+                        const uint32_t bits = left >= 4 ? 32u : (left > 0 ? 8u * (uint32_t)left : 0u);
+                        w4[j] &= (uint32_t)((1ull << bits) - 1ull);
+                    }
+                    lds_write16(p, u32x4{w4[0], w4[1], w4[2], w4[3]});
+                }
+                __syncthreads();
+            };
             // Prologue: tiles 0 .. AHEAD-1 in flight, tile 0 published, tile
             // AHEAD issued into the still unused last buffer.
 #pragma unroll
             for (int p = 0; p < AHEAD; p++) issue_pos(stage_off(p), src_tile(p));
             wait_vmcnt<(AHEAD - 1) * IPT>();
             __syncthreads();
+            clear_k_tail(0);
             issue_pos(stage_off(AHEAD), src_tile(AHEAD));
             read_first(buf(0));
             // Main loop and epilogue (from tile nt - AHEAD on, the issued
@@ -784,6 +828,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                         if (t + 1 < nt) {
                             wait_vmcnt<(AHEAD - 1) * IPT>();  // tile t+1 landed
                             __syncthreads();
+                            clear_k_tail(t + 1);
                             dma_tile = src_tile(t + 1 + AHEAD);  // issued between this step's MFMAs
                             dma_off = stage_off(t + 1 + AHEAD);
                         } else {
@@ -816,16 +861,23 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // lane l of block (mi, ni) holds rows 8*(v/4) + 4*(l/32) + v%4, column l%32.
     // Every tile load has landed by now; saying so with a counted wait keeps
     // the compiler from guarding the stores' address registers (once tile
-    // load destinations) with waits on the stores themselves.  The stores are
-    // non-temporal: C is written once and not read back by this kernel, and
-    // streaming it past the L2 keeps the A and B lines that workgroups still
-    // running read (FP16 / INT8 4096^3: about 1% faster).
+    // load destinations) with waits on the stores themselves.
+    // One store instruction writes 128 contiguous bytes of each of two rows.
+    // When C's rows start on 128-byte lines, those are whole lines and the
+    // stores are non-temporal: C is written once and not read back by this
+    // kernel, and streaming it past the L2 keeps the A and B lines that
+    // workgroups still running read (FP16 / INT8 4096^3: about 1% faster).
+    // Otherwise every 128 bytes straddle two lines, and non-temporal partial
+    // lines reach memory as separate partial writes (INT8 4095^3 with
+    // ldc = 4095: 1427 TOP/s against 2086 with plain stores); plain stores
+    // let the L2 merge them into whole lines first.
     // A bounds-checked kernel stores interior tiles without the per-element
     // test (a uniform branch), so only edge tiles pay for the masking.
     wait_vmcnt<0>();
     out_t *C = (out_t *)(args.C + (int64_t)part * args.part_stride);
+    const bool lines = ((uintptr_t)C & 127) == 0 && ((args.ldc * (int64_t)sizeof(out_t)) & 127) == 0;
     const int col_l = lane & 31, rq = (lane >> 5) * 4;
-    auto store_all = [&](auto masked) __attribute__((always_inline)) {
+    auto store_all = [&](auto masked, auto streaming) __attribute__((always_inline)) {
 #pragma unroll
         for (int mi = 0; mi < G::MI; mi++)
 #pragma unroll
@@ -834,15 +886,30 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int row = m0 + wm * G::WTM + mi * 32 + (v >> 2) * 8 + rq + (v & 3);
-                    if (!decltype(masked)::value || (row < args.M && col < args.N))
-                        __builtin_nontemporal_store(acc[mi][ni][v], &C[(int64_t)row * args.ldc + col]);
+                    if (!decltype(masked)::value || (row < args.M && col < args.N)) {
+                        out_t *p = &C[(int64_t)row * args.ldc + col];
+                        if constexpr (decltype(streaming)::value)
+                            __builtin_nontemporal_store(acc[mi][ni][v], p);
+                        else
+                            *p = acc[mi][ni][v];
+                    }
                 }
             }
     };
-    if (!GUARD || (m0 + BM <= args.M && n0 + BN <= args.N))
-        store_all(std::false_type{});
-    else
-        store_all(std::true_type{});
+    // (The bounds-checked kernels always store plainly: one store form fewer
+    // keeps their register use down, and on the ragged shapes they serve
+    // plain stores measured as fast: FP16 / INT8 4000^3 1157 / 2089 against
+    // 1157 / 2052.)
+    if constexpr (!GUARD) {
+        if (lines)
+            store_all(std::false_type{}, std::true_type{});
+        else
+            store_all(std::false_type{}, std::false_type{});
+    } else if (m0 + BM <= args.M && n0 + BN <= args.N) {
+        store_all(std::false_type{}, std::false_type{});
+    } else {
+        store_all(std::true_type{}, std::false_type{});
+    }
 }
 
 }  // namespace tdg
