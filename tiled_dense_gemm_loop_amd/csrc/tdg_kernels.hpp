@@ -486,6 +486,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             for (int i = 0; i < G::CB; i++) rb[i] = load16_global(src_b[i]);
         }
     };
+    // One chunk of an unchecked register load (d: A chunks first, then B).
+    auto load_one = [&](int kt, int d) __attribute__((always_inline)) {
+        kt = phys(kt);
+        if (d < G::CA) ra[d] = *(const u32x4 *)(a_ptr(kt, d) + a_voff);
+        else rb[d - G::CA] = *(const u32x4 *)(b_ptr(kt, d - G::CA) + b_voff);
+    };
     // Drain staged chunk d (A chunks first, then B) into the buffer at st.
     auto store_one = [&](unsigned char *st, int d) {
         if (d < G::CA) {
@@ -617,8 +623,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // pipe stays busy.
     // With SUB > 1 (FP32) the step's MFMAs go round-robin over the
     // accumulators, so dependent MFMAs are NM instructions apart.
+    // Register-prefetch loop with two buffers on unchecked whole tiles: the
+    // drain of tile t+1 runs in tile t's next-to-last step, and the tile
+    // whose global loads are issued chunk by chunk right after it, as each
+    // staging register is freed (EARLY_REG; see the K loop).
+    constexpr bool EARLY_REG = VAR == VAR_REG && STAGES == 2 && G::KSTEPS >= 4 && !GUARD;
+    int reg_ahead = 0;
     auto step = [&](int cset, const unsigned char *rst, int rstep, int rset, bool reads,
-                    uint32_t dma_st, int dma_kt, bool dma, unsigned char *wst, auto checked) {
+                    uint32_t dma_st, int dma_kt, bool dma, unsigned char *wst, bool drain, auto checked) {
         constexpr int NM = G::MI * G::NI, NR = G::MI + G::NI, ND = G::CA + G::CB;
         constexpr int NMF = NM * MM::SUB;  // MFMA issue slots in the step
 #pragma unroll
@@ -642,11 +654,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 for (int d = (t * ND + NMF - 1) / NMF; d < ((t + 1) * ND + NMF - 1) / NMF; d++)
                     issue_direct_one(dma_st, dma_kt, d, checked);
             }
-            if constexpr (VAR == VAR_REG) {
-                if (wst) {
+            if constexpr (EARLY_REG) {
+                if (drain) {
 #pragma unroll
-                    for (int d = (t * ND + NMF - 1) / NMF; d < ((t + 1) * ND + NMF - 1) / NMF; d++)
+                    for (int d = (t * ND + NMF - 1) / NMF; d < ((t + 1) * ND + NMF - 1) / NMF; d++) {
                         store_one(wst, d);
+                        load_one(reg_ahead, d);  // its staging register is free now
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -684,7 +698,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             const unsigned char *rst = r < G::KSTEPS ? st : next;
             const int rstep = r < G::KSTEPS ? r : r - G::KSTEPS;
             step(set_of(s), rst, rstep, set_of(rstep), true, dma_off, dma_tile,
-                 VAR == VAR_DIRECT && r == G::KSTEPS, s == G::KSTEPS - 2 ? early_st : nullptr,
+                 VAR == VAR_DIRECT && r == G::KSTEPS, early_st, EARLY_REG && s == G::KSTEPS - 2,
                  checked);
         }
     };
@@ -709,19 +723,30 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 compute_tile(smem, [&]() -> const unsigned char * { return smem; }, unchecked_t{});
             }
         } else if constexpr (VAR == VAR_REG) {
-            // Prologue: tile 0 into buffer 0.
-            load_regs(0);
-            store_regs(smem);
-            __syncthreads();
-            read_first(smem);
             // Main loop + epilogue: tile t+1 is in registers (global loads in
             // flight) while tile t is computed; the registers are drained into
             // buffer (t+1) % STAGES at the tile boundary.
-            constexpr bool EARLY = STAGES == 2 && G::KSTEPS >= 4 && !GUARD;
+            // With two buffers on unchecked whole tiles (EARLY_REG), the drain
+            // of tile t+1 is spread over the MFMAs of tile t's next-to-last
+            // step, and each staging register, once drained, at once receives
+            // its chunk of tile t+2: the loads then have a whole tile of MFMAs
+            // to land in, not just the steps before the drain.  The drain and
+            // the loads run in every tile, so that the compiler can count the
+            // loads in flight (a conditional load makes it wait for all of
+            // them): past the end, the last tile is loaded again and drained
+            // into the buffer just freed, which is never read again.
+            constexpr bool EARLY = EARLY_REG;
+            // Prologue: tile 0 into buffer 0 (and, EARLY, tile 1 into registers).
+            load_regs(0);
+            store_regs(smem);
+            __syncthreads();
+            if (EARLY) load_regs(min(1, nt - 1));
+            read_first(smem);
             for (int t = 0; t < nt; t++) {
-                if (t + 1 < nt) load_regs(t + 1);
+                if (!EARLY && t + 1 < nt) load_regs(t + 1);
                 __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-                early_st = EARLY && t + 1 < nt ? buf(t + 1) : nullptr;
+                early_st = EARLY ? buf(t + 1) : nullptr;
+                reg_ahead = min(t + 2, nt - 1);
                 compute_tile(buf(t), [&]() -> const unsigned char * {
                     if (t + 1 < nt) {
                         if (!EARLY) {
