@@ -5,7 +5,9 @@ accumulate, M = N = K = 4096) with the operands already resident in HBM.
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream), bracketing exactly --steps launches after
 --warmup untimed ones ("Analyze Kernel Bottleneck", Step 1: event timing
-after warm-up, effective GFLOPS = 2*M*N*K / t).
+after warm-up, effective GFLOPS = 2*M*N*K / t).  After the warm-ups and a
+synchronize, a ~150 us spin kernel is enqueued before the start event, so
+the timed launches are queued back to back when timing begins.
 
 Printed on stdout: ONE short JSON line with the headline value, the roofline
 object of its kernel (with the metric's three parts -- FP16 and INT8 4096^3
@@ -140,6 +142,18 @@ def launcher(tdg, wl, dA, dB, C, variant: str):
     return lambda: fn(dA, dB, C, cfg=cfg)
 
 
+def hold_stream(us: float = 150.0) -> None:
+    """Enqueue a short spin kernel on the current stream, so that the launches
+    enqueued after it are already queued when the GPU reaches the next event:
+    the timed region then holds only back-to-back kernels, not the host's
+    latency for the first launch after a synchronize (which would be amortised
+    over few launches: ~1.5-3% at 20 of them)."""
+    import torch
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is not None:
+        sleep(int(us * 2400))  # cycles of a clock of about 2.4 GHz or less
+
+
 def time_launches(run, steps: int, warmup: int) -> float:
     """Mean milliseconds per launch over `steps` back-to-back launches,
     bracketed by events on the launching (current) stream."""
@@ -149,6 +163,7 @@ def time_launches(run, steps: int, warmup: int) -> float:
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    hold_stream()
     start.record()
     for _ in range(steps):
         run()
@@ -396,6 +411,20 @@ def cpu_baseline(wl, A, B, target_s: float, part_s: float, part_names):
             "per_config": per}
 
 
+def kernel_record(tdg, wl) -> dict:
+    """The planner's configuration and figures for a workload's pipelined
+    call, beside the HIP runtime's view of that kernel (registers, spills,
+    LDS, resident workgroups per compute unit)."""
+    code = DTYPE_CODE[wl.dtype]
+    cfg, info = tdg.tdg_plan(code, wl.M, wl.N, wl.K)
+    out = {"config": cfg, "plan": info, "resources": None}
+    for i in range(tdg.tdg_config_count(code)):
+        if tdg.tdg_config_at(code, i) == cfg:
+            out["resources"] = tdg.tdg_config_resources(code, i)
+            break
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -557,7 +586,9 @@ def main():
     # Everything else measured goes to stderr and, when asked, to a file: the
     # one stdout line stays short enough to be read whole.
     detail = {"line": line, "measured_ceilings": ceilings, "launches": launches, "cold": cold,
-              "variants": table or None, "transpose_ladder": ladder, "tile_sweep": sweep}
+              "variants": table or None, "transpose_ladder": ladder, "tile_sweep": sweep,
+              "kernels": {name: kernel_record(tdg, si.WORKLOADS[name])
+                          for name in PART_NAMES + ("int8_256", "fp16_1024")}}
     if args.detail_out:
         d = os.path.dirname(os.path.abspath(args.detail_out))
         os.makedirs(d, exist_ok=True)
