@@ -588,13 +588,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // first fragments are then read into their sets, so the tile change
     // costs no exposed LDS latency either.
     static_assert(G::KSTEPS % 2 == 0, "fragment set parity must repeat per tile");
-#ifndef TDG_FRAG_DIST
-#define TDG_FRAG_DIST 2
-#endif
-    // Fragment read distance: 2 K steps ahead for the direct-to-LDS loop when
-    // a tile has 4 steps (one register set per step), else 1 (two sets); the
-    // register-prefetch loop has no room for more sets beside its staging.
-    constexpr int FD = (VAR == VAR_DIRECT && G::KSTEPS == 4) ? TDG_FRAG_DIST : 1;
+    // Fragment read distance: when a tile has 4 K steps, the direct-to-LDS
+    // loop keeps one register set per step and reads 3 steps ahead (2 in its
+    // bounds-checked form, whose address work leaves no registers for the
+    // fourth live set), else 1 (two sets); the register-prefetch loop has no
+    // room for more sets beside its staging.  Reading 3 steps ahead put the
+    // tile boundary, with its wait and barrier, one step earlier, and together
+    // with the copies spread over two steps (below) made the 256 x 256
+    // tiles about 1.5% faster (FP16 and INT8 4096^3).
+    constexpr int FD = (VAR == VAR_DIRECT && G::KSTEPS == 4) ? (GUARD ? 2 : 3) : 1;
     constexpr int NSETS = FD == 1 ? 2 : G::KSTEPS;
     static_assert(FD == 1 || NSETS == G::KSTEPS, "set index must equal the step index");
     u32x4 fa[NSETS][G::MI], fb[NSETS][G::NI];
@@ -614,9 +616,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
         for (int ni = 0; ni < G::NI; ni++) fb[set][ni] = read_bfrag(st, s, ni);
     };
     // One K step's MFMAs with the fragment reads of a later step (read
-    // units: MI A reads, then NI pairs of transposed B reads) and, at a tile
-    // boundary, the DMA instructions of a later tile spread between them:
-    // after MFMA m come the units and DMAs whose even share falls on m.
+    // units: MI A reads, then NI pairs of transposed B reads) and, from the
+    // tile boundary on, DMA instructions [dma_lo, dma_hi) of a later tile
+    // spread between them: after MFMA m come the units and DMAs whose even
+    // share falls on m.
     // Vector-memory and LDS instructions issue in order per wave, so a burst
     // of them from every wave at once queues and holds back each wave's next
     // MFMAs; spread out, each one issues into an idle queue while the MFMA
@@ -630,7 +633,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     constexpr bool EARLY_REG = VAR == VAR_REG && STAGES == 2 && G::KSTEPS >= 4 && !GUARD;
     int reg_ahead = 0;
     auto step = [&](int cset, const unsigned char *rst, int rstep, int rset, bool reads,
-                    uint32_t dma_st, int dma_kt, bool dma, unsigned char *wst, bool drain, auto checked) {
+                    uint32_t dma_st, int dma_kt, int dma_lo, int dma_hi, unsigned char *wst, bool drain,
+                    auto checked) {
         constexpr int NM = G::MI * G::NI, NR = G::MI + G::NI, ND = G::CA + G::CB;
         constexpr int NMF = NM * MM::SUB;  // MFMA issue slots in the step
 #pragma unroll
@@ -649,10 +653,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                     }
                 }
             }
-            if (dma) {
+            if (dma_hi > dma_lo) {
+                const int nd = dma_hi - dma_lo;
 #pragma unroll
-                for (int d = (t * ND + NMF - 1) / NMF; d < ((t + 1) * ND + NMF - 1) / NMF; d++)
-                    issue_direct_one(dma_st, dma_kt, d, checked);
+                for (int d = (t * nd + NMF - 1) / NMF; d < ((t + 1) * nd + NMF - 1) / NMF; d++)
+                    issue_direct_one(dma_st, dma_kt, dma_lo + d, checked);
             }
             if constexpr (EARLY_REG) {
                 if (drain) {
@@ -686,6 +691,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // keeps only the barrier that publishes it.  Measured 1-2% faster on
     // interior tiles; the bounds-checked form keeps the drain at the
     // boundary, where its byte fix-ups cost less than between the MFMAs.
+    // The copies of a later tile go out over SPREAD steps from the boundary
+    // on: two in the unchecked direct-to-LDS loop with a read distance of 2
+    // or more, which halves the vector-memory instructions per step; one in
+    // the bounds-checked form, whose checked copies cost more there (FP16
+    // 4000^3: 5% slower over two steps).  Every copy of the tile is issued
+    // before the next boundary, so the vmcnt counts do not change.
+    constexpr int SPREAD = VAR == VAR_DIRECT && !GUARD && FD >= 2 ? 2 : 1;
+    constexpr int ND_ALL = G::CA + G::CB;
     int dma_tile = 0;
     uint32_t dma_off = 0;
     unsigned char *early_st = nullptr;
@@ -697,9 +710,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             if (r == G::KSTEPS) next = boundary();
             const unsigned char *rst = r < G::KSTEPS ? st : next;
             const int rstep = r < G::KSTEPS ? r : r - G::KSTEPS;
-            step(set_of(s), rst, rstep, set_of(rstep), true, dma_off, dma_tile,
-                 VAR == VAR_DIRECT && r == G::KSTEPS, early_st, EARLY_REG && s == G::KSTEPS - 2,
-                 checked);
+            // the copies of a later tile: DMA instructions [lo, hi) of the step
+            const int part = VAR == VAR_DIRECT && r >= G::KSTEPS && r < G::KSTEPS + SPREAD ? r - G::KSTEPS : -1;
+            const int lo = part < 0 ? 0 : part * ND_ALL / SPREAD;
+            const int hi = part < 0 ? 0 : (part + 1) * ND_ALL / SPREAD;
+            step(set_of(s), rst, rstep, set_of(rstep), true, dma_off, dma_tile, lo, hi, early_st,
+                 EARLY_REG && s == G::KSTEPS - 2, checked);
         }
     };
     using unchecked_t = std::false_type;
