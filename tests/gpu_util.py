@@ -44,28 +44,41 @@ def check_i8(C_gpu, A: np.ndarray, B: np.ndarray):
         len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])])
 
 
-def check_f16(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False):
+# The pages' own acceptance pairs ("Pipeline GPU Kernel", Step 5): absolute
+# and relative 1e-2 for FP16 tensor-core products, 1e-3 for FP32 scalar
+# arithmetic.  They do not say how the two combine; read here as
+# |err| <= abs + rel * |ref|.  The 1e-4 * sum |a b| bound is the acceptance
+# rule; this one is checked beside it on the benchmark's workloads.
+PAGES_RULE = {"f16": (1e-2, 1e-2), "f32": (1e-3, 1e-3)}
+
+
+def _check_float(kind, got, ref, S, exact, pages_rule):
+    err = np.abs(got - ref)
+    tol = 0.0 if exact else 1e-4
+    bad = np.argwhere(err > tol * S)
+    assert bad.size == 0, "%d elements out of tolerance, first at %s: got %r want %r (S=%r)" % (
+        len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])], S[tuple(bad[0])])
+    if pages_rule:
+        a, r = PAGES_RULE[kind]
+        bad = np.argwhere(err > a + r * np.abs(ref))
+        assert bad.size == 0, "%d elements outside the pages' %s rule, first at %s: got %r want %r" % (
+            len(bad), kind, tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+def check_f16(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False, pages_rule: bool = False):
     """FP16 -> FP32 within |err| <= 1e-4 * sum_k |a_ik b_kj| per element
-    (exactly equal when `exact`)."""
+    (exactly equal when `exact`; also within the pages' pair when
+    `pages_rule`)."""
     ref, S = oracle.gemm_f16(A, B)
-    got = C_gpu.cpu().numpy().astype(np.float64)
-    err = np.abs(got - ref)
-    tol = 0.0 if exact else 1e-4
-    bad = np.argwhere(err > tol * S)
-    assert bad.size == 0, "%d elements out of tolerance, first at %s: got %r want %r (S=%r)" % (
-        len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])], S[tuple(bad[0])])
+    _check_float("f16", C_gpu.cpu().numpy().astype(np.float64), ref, S, exact, pages_rule)
 
 
-def check_f32(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False):
+def check_f32(C_gpu, A: np.ndarray, B: np.ndarray, exact: bool = False, pages_rule: bool = False):
     """FP32 -> FP32 within |err| <= 1e-4 * sum_k |a_ik b_kj| per element
-    (exactly equal when `exact`)."""
+    (exactly equal when `exact`; also within the pages' pair when
+    `pages_rule`)."""
     ref, S = oracle.gemm_f32(A, B)
-    got = C_gpu.cpu().numpy().astype(np.float64)
-    err = np.abs(got - ref)
-    tol = 0.0 if exact else 1e-4
-    bad = np.argwhere(err > tol * S)
-    assert bad.size == 0, "%d elements out of tolerance, first at %s: got %r want %r (S=%r)" % (
-        len(bad), tuple(bad[0]), got[tuple(bad[0])], ref[tuple(bad[0])], S[tuple(bad[0])])
+    _check_float("f32", C_gpu.cpu().numpy().astype(np.float64), ref, S, exact, pages_rule)
 
 
 def sample_indices(M: int, N: int, count: int, seed: int, tile_m: int = 256, tile_n: int = 256):

@@ -41,13 +41,13 @@ def _operands(dtype, M, N, K, seed, dist="normal"):
     return si.f16_normal(M, K, seed), si.f16_normal(K, N, seed + 1)
 
 
-def _check(dtype, C, A, B, exact=False):
+def _check(dtype, C, A, B, exact=False, pages_rule=False):
     if dtype == I8:
         check_i8(C, A, B)
     elif dtype == F32:
-        check_f32(C, A, B, exact=exact)
+        check_f32(C, A, B, exact=exact, pages_rule=pages_rule)
     else:
-        check_f16(C, A, B, exact=exact)
+        check_f16(C, A, B, exact=exact, pages_rule=pages_rule)
 
 
 def _variants(lib, dtype, tile):
@@ -840,8 +840,9 @@ def test_binding_rejects_host_tensors(lib):
 def test_full_size_whole_output(lib, name):
     """The benchmark's workloads in the configuration it times: every element
     of C against the oracle (INT8 bit for bit, FP16 / FP32 within
-    1e-4 * sum |a b|), after a quick check of sampled elements (tile corners
-    included) that gives an early, readable failure.  The sequential loop and
+    1e-4 * sum |a b| and within the pages' own absolute / relative pair),
+    after a quick check of sampled elements (tile corners included) that
+    gives an early, readable failure.  The sequential loop and
     every other built loop form at the planner's tile must then equal the
     pipelined output bit for bit ("Pipeline GPU Kernel", Step 5: check a small
     size, then the target size, against the CPU reference)."""
@@ -853,7 +854,7 @@ def test_full_size_whole_output(lib, name):
     rows, cols = sample_indices(wl.M, wl.N, 3000, seed=wl.seed_a, tile_n=min(256, wl.N))
     C_pipe = gemm(lib, dtype, "pipelined", dA, dB)
     check_sampled(C_pipe, dtype, A, B, rows, cols)
-    _check(dtype, C_pipe, A, B)
+    _check(dtype, C_pipe, A, B, pages_rule=True)
     C_single = gemm(lib, dtype, "single", dA, dB)
     assert torch.equal(C_pipe, C_single)
     tile, _ = lib.tdg_plan(CODE[dtype], wl.M, wl.N, wl.K)
