@@ -135,10 +135,12 @@ def recommendations(wl: str, line: dict, part: dict, kern: dict, prof: dict, cei
         fill = prof["vmem_rd"] * 1024.0 / NUM_CU / cycles
         need = plan["need_bytes_per_clk"]
         gain = max(0.0, 1.0 - fill / need) if util is None else max(0.0, min(1.0 - util, 1.0 - fill / need))
-        recs.append((gain, "L2 -> LDS fill: the tile stream moves %.1f B per clock per CU (counted 16-byte wave "
-                           "loads over the active cycles) against the %.0f B the %dx%d tile needs at the full MFMA "
-                           "rate; L2 hit rate %.1f%%, A + B fetched %.2fx.  More operations per byte per CU (a "
-                           "larger tile) or fewer L2 misses per CU would lift it; up to %.0f%%." % (
+        recs.append((gain, "L2 -> LDS fill: averaged over the launch, the tile stream moves %.1f B per clock per "
+                           "CU (counted 16-byte wave loads over the active cycles) against the %.0f B the %dx%d "
+                           "tile needs at the full MFMA rate; L2 hit rate %.1f%%, A + B fetched %.2fx.  The average "
+                           "includes the prologue and the C write, when no tile is copied, and the fill's share "
+                           "cannot exceed the cycles the matrix cores are idle, so %.0f%% is a bound, not an "
+                           "estimate.  More operations per byte per CU (a larger tile) would lower the need." % (
                                fill, need, kern["config"]["bm"], kern["config"]["bn"], 100 * prof.get("l2_hit", 0),
                                prof.get("refetch", float("nan")), 100 * gain)))
     c_share = M * N * 4 / (prof.get("traffic") or alg)
