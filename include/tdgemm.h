@@ -45,17 +45,23 @@
  * kernel cannot reach its rows returns TDG_ERR_UNSUPPORTED.
  * Degenerate shapes: M == 0 or N == 0 returns TDG_OK and launches nothing;
  * K == 0 writes zeros to C.
- * Any shape and alignment is accepted.  The fast path needs 16-byte aligned
- * A and B, lda and ldb whole multiples of 16 bytes and M, N, K whole multiples
- * of the tile.  A ragged shape with the same alignment and with N and K whole
- * multiples of 16 bytes (8 FP16 or 16 INT8 elements) keeps the direct-to-LDS
- * copy: chunks outside A or B are fetched from a zero block and stores are
- * masked.  Anything else runs the bounds-checked register-prefetch form of
- * the same kernel: one 16-byte load per chunk at any byte alignment, with
- * rows outside the operand read from a zero block and K tails zeroed
- * ("Pipeline GPU Kernel", Common Pitfalls: boundary handling with async
- * copies).  No load reaches past the 4 KiB page of a byte of A or B, so the
- * operands need no padding.
+ * Any shape and alignment is accepted.  Whole tiles (M, N, K multiples of
+ * the tile) run the unchecked kernels: the direct-to-LDS loop at any
+ * alignment (its DMA reads 16 bytes from any byte address), the register and
+ * sequential loops with 16-byte aligned A and B and lda, ldb multiples of 16
+ * bytes.  Ragged shapes run the bounds-checked direct-to-LDS loop: chunks
+ * sit on a 16-byte grid from each row's first byte, those that start outside
+ * A or B are fetched from a zero block, those that start inside are fetched
+ * whole (A's bytes at k >= K are then cleared in LDS), and stores are
+ * masked.  When the chunk holding an operand's last byte would reach into
+ * another 4 KiB page, the bounds-checked register-prefetch form runs
+ * instead: one 16-byte load per chunk at any byte alignment, partial chunks
+ * that would leave their page loaded end-anchored and shifted ("Pipeline GPU
+ * Kernel", Common Pitfalls: boundary handling with async copies).
+ * tdg_plan_operands tells which form a call runs.  Reads stay inside each
+ * operand's span -- from its first byte through the 4 KiB page of its last
+ * byte, rows and the gaps between them (one allocation, as for any strided
+ * view) -- so the operands need no padding.
  * Errors: TDG_ERR_NO_DEVICE when the current device is not gfx950 or no
  * device is present; TDG_ERR_UNSUPPORTED for an explicit configuration that is
  * not built in or does not fit the device; TDG_ERR_LAUNCH when the launch
@@ -248,6 +254,24 @@ int tdg_splitk_plan(int dtype, int64_t M, int64_t N, int64_t K, int *parts,
  * *out and its figures to *info (either may be NULL).  Host-only
  * arithmetic: needs no device. */
 int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_plan_info *info);
+
+/* The configuration and form that a _pipelined call (or, with a request in
+ * *out, an _ex call) would run on these very operands: tdg_plan judges dense
+ * operands at 16-byte aligned addresses, while the caller's addresses and
+ * leading dimensions decide the forms.  Whole tiles run unchecked in the
+ * direct-to-LDS loop at any alignment (its DMA reads 16 bytes from any byte
+ * address); the register and sequential loops run unchecked only with
+ * 16-byte aligned rows.  Ragged shapes run the bounds-checked direct-to-LDS
+ * loop, except when an operand's last 16-byte chunk (chunks sit on a 16-byte
+ * grid from each row's first byte) reaches into a 4 KiB page beyond the
+ * operand: that page need not be mapped, and the bounds-checked
+ * register-prefetch loop runs instead ("Pipeline GPU Kernel", Common
+ * Pitfalls: asynchronous copies need valid sources).  info->guarded gives
+ * the form.  A and B are compared, never dereferenced: host-only.
+ * TDG_ERR_INVALID_ARG for a bad dtype or size, a leading dimension below
+ * the row length, or a NULL operand that is not empty. */
+int tdg_plan_operands(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                      const void *B, int64_t ldb, tdg_config *out, tdg_plan_info *info);
 
 /* The planner's predicted kernel time, in microseconds, of one row of its
  * measured-time table -- a built direct-to-LDS configuration with a 128-byte

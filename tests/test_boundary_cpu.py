@@ -292,17 +292,17 @@ def test_planner_choices():
     assert info["grid"] == 256 and info["guarded"] == 0
     cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 16384, 64, 8192)
     assert cfg["bn"] == 64 and cfg["lds_stages"] >= 2 and info["grid"] >= 256
-    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_I8I32, 300, 290, 333)
-    assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH
-    # ragged, but N and K whole 16-byte chunks: the copy stays in the DMA
+    # ragged shapes keep the copy in the DMA's bounds-checked form, whether
+    # or not N and K are whole 16-byte chunks (dense operands: rows off the
+    # 16-byte grid when they are not)
     for code, M, N, K in [(0, 300, 264, 200), (0, 4000, 4000, 4000), (1, 300, 272, 144),
-                          (0, 16383, 64, 8192), (1, 1, 16, 272)]:
+                          (0, 16383, 64, 8192), (1, 1, 16, 272), (1, 300, 290, 333),
+                          (0, 300, 264, 201), (0, 300, 260, 200), (1, 300, 272, 136)]:
         cfg, info = tdg.tdg_plan(code, M, N, K)
         assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS, (M, N, K)
-    # a K or N that splits a 16-byte chunk takes the guarded register-prefetch loop
-    for code, M, N, K in [(0, 300, 264, 201), (0, 300, 260, 200), (1, 300, 272, 136)]:
-        cfg, info = tdg.tdg_plan(code, M, N, K)
-        assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH, (M, N, K)
+    # one K tile: nothing to overlap, the sequential loop
+    cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 300, 264, 33)
+    assert cfg["variant"] == tdg.TDG_VARIANT_SINGLE and info["pipelined"] == 0
     # the 4000^3 plan keeps the 256x256 tile of the 4096^3 one
     cfg, _ = tdg.tdg_plan(tdg.TDG_DTYPE_F16F32, 4000, 4000, 4000)
     assert (cfg["bm"], cfg["bn"]) == (256, 256)
@@ -313,7 +313,7 @@ def test_planner_choices():
     cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F32F32, 300, 260, 200)
     assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS
     cfg, info = tdg.tdg_plan(tdg.TDG_DTYPE_F32F32, 300, 262, 200)
-    assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_REG_PREFETCH
+    assert info["guarded"] == 1 and cfg["variant"] == tdg.TDG_VARIANT_DIRECT_LDS
     # every built configuration can be planned back exactly
     for code in (0, 1, 2):
         for i in range(tdg.tdg_config_count(code)):
@@ -529,3 +529,109 @@ def test_config_resources_validation():
     assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, n, ctypes.byref(r)) == tdg.TDG_ERR_INVALID_ARG
     assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, 0, None) == tdg.TDG_ERR_INVALID_ARG
     assert lib.tdg_config_resources(tdg.TDG_DTYPE_F16F32, 0, ctypes.byref(r)) == tdg.TDG_ERR_NO_DEVICE
+
+
+# --- which loop a call on given operands runs (tdg_plan_operands) ------------
+
+ES = {tdg.TDG_DTYPE_F16F32: 2, tdg.TDG_DTYPE_I8I32: 1, tdg.TDG_DTYPE_F32F32: 4}
+BASE = 1 << 40          # an address on a 4 KiB page boundary; never dereferenced
+
+
+def _form(dtype, M, N, K, a, lda, b, ldb, **req):
+    cfg, info = tdg.tdg_plan_operands(dtype, M, N, K, a, lda, b, ldb, tdg.TdgConfig(**req) if req else None)
+    return cfg["variant"], info["guarded"]
+
+
+def _last_chunk_leaves_page(base, rows, ld, cols, es):
+    """Walk the last row's 16-byte chunks from its first byte, as the copy
+    does, and say whether the one holding the operand's last byte reads a
+    byte past it in another 4 KiB page (bytes before it are the operand's)."""
+    row = base + (rows - 1) * ld * es
+    last = row + cols * es - 1
+    start = row
+    while start + 16 <= last:          # the chunk [start, start + 16) ends before the last byte
+        start += 16
+    return any((x >> 12) != (last >> 12) for x in range(last + 1, start + 16))
+
+
+@pytest.mark.parametrize("dtype", sorted(ES))
+def test_plan_operands_whole_tiles_run_the_dma_at_any_alignment(dtype):
+    """Whole tiles: the direct-to-LDS loop runs unchecked whatever the rows'
+    alignment; the register and sequential loops run unchecked only with
+    16-byte aligned rows."""
+    es = ES[dtype]
+    M = N = K = 1024
+    aligned = (BASE, K, BASE + (1 << 30), N)
+    for a_off, lda in ((es, K + 1), (0, K + 1), (es, K)):
+        odd = (BASE + a_off, lda, BASE + (1 << 30) + es, N + 3)
+        assert _form(dtype, M, N, K, *aligned) == (tdg.TDG_VARIANT_DIRECT_LDS, 0)
+        assert _form(dtype, M, N, K, *odd) == (tdg.TDG_VARIANT_DIRECT_LDS, 0)
+        for v in (tdg.TDG_VARIANT_REG_PREFETCH, tdg.TDG_VARIANT_SINGLE):
+            stages = 2 if v == tdg.TDG_VARIANT_REG_PREFETCH else 1
+            assert _form(dtype, M, N, K, *aligned, variant=v, lds_stages=stages) == (v, 0)
+            assert _form(dtype, M, N, K, *odd, variant=v, lds_stages=stages) == (v, 1)
+    # the dense, aligned case is what tdg_plan assumes
+    cfg, info = tdg.tdg_plan(dtype, M, N, K)
+    cfg2, info2 = tdg.tdg_plan_operands(dtype, M, N, K, *aligned)
+    assert cfg == cfg2 and info == info2
+
+
+@pytest.mark.parametrize("dtype", sorted(ES))
+def test_plan_operands_last_chunk_page_rule(dtype):
+    """Ragged shapes with rows off the 16-byte grid: the bounds-checked
+    direct-to-LDS loop, unless the chunk holding an operand's last byte
+    reaches into another page, when the register-prefetch loop runs.  Every
+    placement of A, then of B, within a page, against a walk of the chunks."""
+    es = ES[dtype]
+    M, N, K = 300, 270, 137                      # K and N end inside a chunk
+    lda, ldb = K + 1, N + 1
+    b_far, a_far = BASE + (1 << 32), BASE + (1 << 33)
+    seen = set()
+    for s in range(0, 4096, es):
+        a = BASE + s
+        want = tdg.TDG_VARIANT_REG_PREFETCH if _last_chunk_leaves_page(a, M, lda, K, es) \
+            else tdg.TDG_VARIANT_DIRECT_LDS
+        b_ok = not _last_chunk_leaves_page(b_far, K, ldb, N, es)
+        assert b_ok
+        assert _form(dtype, M, N, K, a, lda, b_far, ldb) == (want, 1), s
+        seen.add(want)
+        b = BASE + s
+        want = tdg.TDG_VARIANT_REG_PREFETCH if _last_chunk_leaves_page(b, K, ldb, N, es) \
+            else tdg.TDG_VARIANT_DIRECT_LDS
+        assert not _last_chunk_leaves_page(a_far, M, lda, K, es)
+        assert _form(dtype, M, N, K, a_far, lda, b, ldb) == (want, 1), s
+        seen.add(want)
+    assert seen == {tdg.TDG_VARIANT_REG_PREFETCH, tdg.TDG_VARIANT_DIRECT_LDS}
+
+
+@pytest.mark.parametrize("dtype", sorted(ES))
+def test_plan_operands_aligned_rows_always_keep_the_dma(dtype):
+    """With 16-byte aligned rows no chunk leaves its page: every ragged shape
+    (K > 0, at least two K tiles) runs the direct-to-LDS loop, wherever on a
+    page the operands sit."""
+    import random
+    es = ES[dtype]
+    rng = random.Random(7 + dtype)
+    epc = 16 // es
+    for _ in range(300):
+        M, N, K = rng.randint(1, 900), rng.randint(1, 900), rng.randint(300, 900)
+        lda = -(-K // epc) * epc + epc * rng.randint(0, 3)
+        ldb = -(-N // epc) * epc + epc * rng.randint(0, 3)
+        a = BASE + 16 * rng.randint(0, 255)
+        b = BASE + (1 << 32) + 16 * rng.randint(0, 255)
+        assert _form(dtype, M, N, K, a, lda, b, ldb)[0] == tdg.TDG_VARIANT_DIRECT_LDS, (M, N, K)
+
+
+def test_plan_operands_rejects_bad_arguments():
+    f16 = tdg.TDG_DTYPE_F16F32
+    for args in ((f16, 64, 64, 64, BASE, 63, BASE, 64),       # lda < K
+                 (f16, 64, 64, 64, BASE, 64, BASE, 63),       # ldb < N
+                 (f16, 64, 64, 64, 0, 64, BASE, 64),          # NULL A
+                 (f16, 64, 64, 64, BASE, 64, 0, 64),          # NULL B
+                 (f16, -1, 64, 64, BASE, 64, BASE, 64),
+                 (9, 64, 64, 64, BASE, 64, BASE, 64)):
+        with pytest.raises(tdg.TdgError) as e:
+            tdg.tdg_plan_operands(*args)
+        assert e.value.status == tdg.TDG_ERR_INVALID_ARG
+    # empty operands may be NULL
+    tdg.tdg_plan_operands(f16, 0, 64, 64, 0, 64, BASE, 64)

@@ -349,6 +349,136 @@ def test_split_chunk_direct_every_tile_and_ring(lib, dtype):
                 assert torch.equal(ref_out, C2), "%s differs under the LDS poison" % name
 
 
+# --- rows off the 16-byte grid: the direct-to-LDS loop -----------------------
+
+def _misaligned_operands(dtype, M, N, K, seed, shift=1):
+    """Operands whose rows start off the 16-byte grid: leading dimensions of
+    K + 1 and N + 1 elements, bases `shift` elements into their buffers,
+    everything around them POISON."""
+    A, B = _operands(dtype, M, N, K, seed)
+    lda, ldb = K + 1, N + 1
+    bigA = np.full(M * lda + shift + 16, POISON[dtype], dtype=A.dtype)
+    bigB = np.full(K * ldb + shift + 16, POISON[dtype], dtype=B.dtype)
+    bigA[shift:shift + M * lda].reshape(M, lda)[:, :K] = A
+    bigB[shift:shift + K * ldb].reshape(K, ldb)[:, :N] = B
+    dA = to_device(bigA)[shift:shift + M * lda].view(M, lda)[:, :K]
+    dB = to_device(bigB)[shift:shift + K * ldb].view(K, ldb)[:, :N]
+    return A, B, dA, dB
+
+
+def _dma_placement(lib, dtype, M, N, K, seed):
+    """Misaligned operands that the pipelined call runs in the direct-to-LDS
+    loop (a base shift for which neither operand's last chunk leaves its
+    page: all but about 1 in 250 placements)."""
+    code = CODE[dtype]
+    for shift in (1, 2, 3, 5):
+        A, B, dA, dB = _misaligned_operands(dtype, M, N, K, seed, shift)
+        cfg, info = lib.tdg_plan_operands(code, M, N, K, dA.data_ptr(), dA.stride(0),
+                                          dB.data_ptr(), dB.stride(0))
+        if cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS:
+            assert dA.data_ptr() % 16 or dA.stride(0) * dA.element_size() % 16
+            return A, B, dA, dB, cfg, info
+    raise AssertionError("no placement keeps the copy in the DMA")
+
+
+MISALIGNED = [(512, 512, 512), (256, 512, 1024), (300, 270, 137), (257, 129, 263), (1000, 61, 1001),
+              (64, 64, 129)]
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+@pytest.mark.parametrize("M,N,K", MISALIGNED)
+def test_misaligned_rows_run_the_dma(lib, dtype, M, N, K):
+    """Rows off the 16-byte grid (odd leading dimensions, bases off a chunk):
+    the pipelined call runs the direct-to-LDS loop -- unchecked on whole
+    tiles, bounds-checked on ragged shapes -- whose DMA reads each chunk
+    from its own byte address.  Against the oracle, and bit for bit against
+    the bounds-checked register-prefetch loop at the same tile."""
+    import torch
+    A, B, dA, dB, cfg, info = _dma_placement(lib, dtype, M, N, K, seed=M + N + K)
+    whole = M % cfg["bm"] == 0 and N % cfg["bn"] == 0 and K % cfg["bk"] == 0
+    assert info["guarded"] == (0 if whole else 1)
+    C = gemm(lib, dtype, "pipelined", dA, dB)
+    _check(dtype, C, A, B)
+    reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
+    assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_misaligned_rows_every_tile_and_ring(lib, dtype):
+    """Misaligned rows, a long K and an N that end inside a chunk: every
+    tile and every ring depth built against the oracle and bit for bit
+    against the tile's sequential loop; the direct-to-LDS forms once more
+    under the LDS poisoning race screen."""
+    import torch
+    M, N, K = 300, 270, {F16: 2001, I8: 4013, F32: 1001}[dtype]
+    A, B, dA, dB, _, _ = _dma_placement(lib, dtype, M, N, K, seed=98)
+    for tile in _tiles(CODE[dtype]):
+        ref_out = None
+        for name, cfg in _variants(lib, dtype, tile):
+            C = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+            if ref_out is None:
+                _check(dtype, C, A, B)
+                ref_out = C
+            else:
+                assert torch.equal(ref_out, C), "%s differs at tile %s" % (name, tile)
+            if cfg["variant"] == lib.TDG_VARIANT_DIRECT_LDS:
+                prev = lib.tdg_set_debug_flags(lib.TDG_DEBUG_POISON_LDS)
+                try:
+                    C2 = gemm(lib, dtype, "ex", dA, dB, cfg=cfg)
+                finally:
+                    lib.tdg_set_debug_flags(prev)
+                assert torch.equal(ref_out, C2), "%s differs under the LDS poison" % name
+
+
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+@pytest.mark.parametrize("which", ["A", "B"])
+def test_last_chunk_across_a_page(lib, dtype, which):
+    """An operand placed so that the 16-byte chunk holding its last byte
+    reaches into the next 4 KiB page: the call runs the bounds-checked
+    register-prefetch loop (tdg_plan_operands says so), whose loads stay in
+    the page of their first byte; placed so that it does not, the
+    direct-to-LDS loop.  Both against the oracle.  The operand sits inside a
+    larger buffer, so every page here is mapped whatever the planner
+    decides; the other operand has aligned rows."""
+    import torch
+    code = CODE[dtype]
+    es = {F16: 2, I8: 1, F32: 4}[dtype]
+    epc = 16 // es
+    M, N, K = 300, 270, 137
+    A, B = _operands(dtype, M, N, K, seed=99)
+    if which == "A":
+        rows, ld, cols, src, other_np, o_cols = M, K + 1, K, A, B, N
+    else:
+        rows, ld, cols, src, other_np, o_cols = K, N + 1, N, B, A, K
+    o_ld = -(-o_cols // epc) * epc             # aligned rows for the other operand
+    o_host = np.full((other_np.shape[0], o_ld), POISON[dtype], dtype=other_np.dtype)
+    o_host[:, :o_cols] = other_np
+    other = to_device(o_host)[:, :o_cols]
+    span = rows * ld
+    big = np.full(span + 2 * 4096 // es, POISON[dtype], dtype=src.dtype)
+    d_big = to_device(big)
+
+    def operands(s):
+        view = d_big[s:s + span].view(rows, ld)[:, :cols]
+        return (view, other) if which == "A" else (other, view)
+
+    found = {}
+    for s in range(4096 // es):
+        a, b = operands(s)
+        cfg, _ = lib.tdg_plan_operands(code, M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0))
+        found.setdefault(cfg["variant"], s)
+    assert set(found) == {lib.TDG_VARIANT_REG_PREFETCH, lib.TDG_VARIANT_DIRECT_LDS}, found
+    for want, s in sorted(found.items()):
+        host = big.copy()
+        host[s:s + span].reshape(rows, ld)[:, :cols] = src
+        d_big.copy_(to_device(host))           # same buffer, same addresses
+        a, b = operands(s)
+        cfg, _ = lib.tdg_plan_operands(code, M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0))
+        assert cfg["variant"] == want, (s, cfg)
+        _check(dtype, gemm(lib, dtype, "pipelined", a, b), A, B)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("dtype", [F16, I8])
 def test_split_chunk_direct_rotated_and_split_k(lib, dtype):
     """The straddling K tile at every position of a rotated K walk (a skinny
@@ -416,8 +546,10 @@ def test_strided_and_misaligned_operands(lib, dtype):
 def test_every_byte_alignment(lib, dtype):
     """Odd leading dimensions, so rows start at every element offset within
     a 16-byte chunk, and every base offset within a chunk; K and N split a
-    chunk, so the tails end at every position.  Whole chunks take the single
-    unaligned load, partial ones the shifted pair of aligned loads."""
+    chunk, so the tails end at every position.  In the register loops (the
+    single-buffer call) whole chunks take the single unaligned load, partial
+    ones the shifted pair of aligned loads; the pipelined call's DMA reads
+    every chunk from its own byte address."""
     epc = 16 // {F16: 2, I8: 1, F32: 4}[dtype]
     M, N, K = 70, 46, 262                     # K, N even; both split a chunk
     bigA, bigB = _operands(dtype, M + 1, N + 2 * epc + 1, K + 2 * epc + 1, seed=17)
@@ -443,8 +575,10 @@ def test_every_byte_alignment(lib, dtype):
 def test_tails_at_every_page_offset(lib, dtype):
     """Odd leading dimensions over enough rows put the partial K
     chunks of A and the partial N chunks of B at every element offset within
-    a 4 KiB page, so some of them would run past their page: those take the
-    pair of aligned loads instead of the single unaligned one."""
+    a 4 KiB page, so some of them would run past their page: in the
+    register loops those take the pair of aligned loads instead of the
+    single unaligned one; the DMA reads them whole (past a row's end lies
+    the next row)."""
     M, N, K = (4200, 46, 4202) if dtype == I8 else (2100, 46, 2102)   # rows cover every offset
     bigA, bigB = _operands(dtype, M, N + 17, K + 1, seed=23)      # lda = K+1, ldb = N+17: odd
     A, B = bigA[:, :K], bigB[:K, :N]
@@ -868,22 +1002,28 @@ def test_full_size_whole_output(lib, name):
                                          (F32, 4095, 4095, 4095)])
 def test_large_odd_whole_output(lib, dtype, M, N, K):
     """Odd sizes near the benchmark sizes: most rows start off a 16-byte
-    boundary, so the planner takes the guarded register-prefetch loop; every
-    element against the oracle (sampled tile edges first, for an early
-    failure message), and the whole output against the guarded sequential
-    loop bit for bit."""
+    boundary, and the planner keeps the bounds-checked direct-to-LDS loop
+    (or, when an operand's last chunk would leave its page, the
+    bounds-checked register-prefetch loop); every element against the
+    oracle (sampled tile edges first, for an early failure message), and
+    the whole output bit for bit against the guarded sequential and
+    register-prefetch loops."""
     import torch
     A, B = _operands(dtype, M, N, K, seed=M + 7)
     dA, dB = to_device(A), to_device(B)
     code = CODE[dtype]
-    cfg, info = lib.tdg_plan(code, M, N, K)
-    assert info["guarded"] == 1 and cfg["variant"] == lib.TDG_VARIANT_REG_PREFETCH
+    cfg, info = lib.tdg_plan_operands(code, M, N, K, dA.data_ptr(), dA.stride(0), dB.data_ptr(),
+                                      dB.stride(0))
+    assert info["guarded"] == 1
+    assert cfg["variant"] in (lib.TDG_VARIANT_DIRECT_LDS, lib.TDG_VARIANT_REG_PREFETCH)
     rows, cols = sample_indices(M, N, 2000, seed=M, tile_m=cfg["bm"], tile_n=cfg["bn"])
     C = gemm(lib, dtype, "pipelined", dA, dB)
     check_sampled(C, dtype, A, B, rows, cols)
     _check(dtype, C, A, B)
     single = dict(cfg, variant=lib.TDG_VARIANT_SINGLE, lds_stages=1)
     assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=single))
+    reg = dict(cfg, variant=lib.TDG_VARIANT_REG_PREFETCH, lds_stages=2)
+    assert torch.equal(C, gemm(lib, dtype, "ex", dA, dB, cfg=reg))
     del C, dA, dB
     torch.cuda.empty_cache()
 

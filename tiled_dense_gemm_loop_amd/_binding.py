@@ -47,7 +47,7 @@ TRANSPOSE_NAMES = {1: "naive", 2: "lds", 3: "lds_padded", 4: "lds_swizzled", 5: 
 EXPORTED = (
     "gemm_f16f32", "gemm_i8i32", "gemm_f16f32_pipelined", "gemm_i8i32_pipelined",
     "gemm_f16f32_ex", "gemm_i8i32_ex", "gemm_f32f32", "gemm_f32f32_pipelined", "gemm_f32f32_ex",
-    "tdg_plan", "tdg_tile_figures", "tdg_config_count",
+    "tdg_plan", "tdg_plan_operands", "tdg_tile_figures", "tdg_config_count",
     "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
     "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
     "gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk", "tdg_splitk_plan",
@@ -123,6 +123,9 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_plan.argtypes = [c_int, i64, i64, i64, ctypes.POINTER(TdgConfig),
                              ctypes.POINTER(TdgPlanInfo)]
     lib.tdg_plan.restype = c_int
+    lib.tdg_plan_operands.argtypes = [c_int, i64, i64, i64, ctypes.c_void_p, i64, ctypes.c_void_p, i64,
+                                      ctypes.POINTER(TdgConfig), ctypes.POINTER(TdgPlanInfo)]
+    lib.tdg_plan_operands.restype = c_int
     lib.tdg_tile_figures.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, i64, i64,
                                      i64, ctypes.POINTER(TdgPlanInfo)]
     lib.tdg_tile_figures.restype = c_int
@@ -344,6 +347,19 @@ def tdg_plan(dtype: int, M: int, N: int, K: int, cfg=None):
     rc = load_library().tdg_plan(dtype, M, N, K, ctypes.byref(c), ctypes.byref(info))
     if rc != TDG_OK:
         raise TdgError(rc, "tdg_plan")
+    return c.as_dict(), info.as_dict()
+
+
+def tdg_plan_operands(dtype: int, M: int, N: int, K: int, a_addr: int, lda: int, b_addr: int, ldb: int,
+                      cfg=None):
+    """(config dict, plan-info dict) a call on operands at these addresses
+    and leading dimensions would run; the addresses are only compared."""
+    c = _cfg(cfg) or TdgConfig()
+    info = TdgPlanInfo()
+    rc = load_library().tdg_plan_operands(dtype, M, N, K, ctypes.c_void_p(a_addr), lda,
+                                          ctypes.c_void_p(b_addr), ldb, ctypes.byref(c), ctypes.byref(info))
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_plan_operands")
     return c.as_dict(), info.as_dict()
 
 

@@ -144,19 +144,45 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Whether the unguarded fast path may run: whole tiles, 16-byte aligned
 // operands and rows, and per-tile offsets inside 32 bits.
-bool fast_ok(const KernelEntry &e, int64_t M, int64_t N, int64_t K, bool vec_ok) {
+// A shape of whole tiles: M, N and K multiples of the tile, so every row
+// of a K tile is whole 16-byte chunks and no chunk runs past its row.  The
+// unchecked direct-to-LDS loop serves it at any alignment: the LDS DMA reads
+// its 16 bytes from any byte address (checked on the GPU for every offset
+// 0..15).  The unchecked register and sequential loops load through 16-byte
+// vector types and also need 16-byte aligned rows (aligned_operands).
+bool fast_ok(const KernelEntry &e, int64_t M, int64_t N, int64_t K) {
     const int bk = cfg_bk(e);
-    if (K == 0 || M % e.bm || N % e.bn || K % bk) return false;
-    return vec_ok;
+    return K > 0 && M % e.bm == 0 && N % e.bn == 0 && K % bk == 0;
 }
 
-// Whether the bounds-checked direct-to-LDS loop may run on a ragged shape:
-// with 16-byte aligned operands and rows every 16-byte chunk starts on a
-// 16-byte boundary, so it lies in one page; chunks that start outside an
-// operand are fetched from a zero block, those that start inside are
-// fetched whole (the kernel clears A's bytes at k >= K when K splits a
-// chunk; B's bytes past N feed only C columns that are not stored).
-bool edge_ok(int64_t K, bool vec_ok) { return vec_ok && K > 0; }
+// Whether the chunk that holds an operand's last byte (rows x cols elements
+// of es bytes, leading dimension ld) reaches into another 4 KiB page.
+// Chunks sit on a 16-byte grid from each row's first byte, so that chunk
+// starts at the last row's first byte plus the last byte's offset rounded
+// down to 16.  With 16-byte aligned rows it never does.
+bool end_chunk_crosses_page(const void *base, int64_t rows, int64_t ld, int64_t cols, int es) {
+    if (rows <= 0 || cols <= 0) return false;
+    const uintptr_t row = (uintptr_t)base + (uintptr_t)((rows - 1) * ld * es);
+    const uintptr_t last = row + (uintptr_t)(cols * es - 1);             // the last byte
+    const uintptr_t start = row + ((uintptr_t)(cols * es - 1) & ~(uintptr_t)15);
+    return ((start + 15) >> 12) != (last >> 12);
+}
+
+// The bounds-checked direct-to-LDS loop runs ragged shapes at any
+// alignment: chunks that start outside an operand are fetched from a zero
+// block and those that start inside are fetched whole; the kernel clears
+// A's bytes at k >= K when K splits a chunk (B's bytes past N feed only C
+// columns that are not stored).  A chunk read whole can run past the
+// operand's end only at the end of its last row, and must not enter a page
+// that holds no byte of the operand (such a page need not be mapped):
+// whether both operands' last chunks stay in their pages.  Operands placed
+// otherwise are left to the bounds-checked register loop, whose loads stay
+// in the page of their first byte.
+bool ends_in_page(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                  int64_t ldb) {
+    const int es = elem_size(dtype);
+    return !end_chunk_crosses_page(A, M, lda, K, es) && !end_chunk_crosses_page(B, K, ldb, N, es);
+}
 
 bool aligned_operands(int dtype, const void *A, int64_t lda, const void *B, int64_t ldb) {
     const int es = elem_size(dtype);
@@ -466,8 +492,9 @@ struct Resolved {
 };
 
 // Complete a (possibly partial) request into a runnable kernel.
+// `end_ok`: the operands' last chunks stay in their pages (ends_in_page).
 int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-            int64_t ldb, const tdg_config &req_in, bool pipelined_default, Resolved *out,
+            int64_t ldb, bool end_ok, const tdg_config &req_in, bool pipelined_default, Resolved *out,
             tdg_config *cfg_out, tdg_plan_info *info) {
     tdg_config req = req_in;
     if (req.variant < 0 || req.variant > TDG_VARIANT_DIRECT_LDS) return TDG_ERR_INVALID_ARG;
@@ -484,8 +511,8 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         return 2;
     };
     const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
-    const bool fast = fast_ok(*tile, M, N, K, vec_ok);
-    const bool edge = !fast && edge_ok(K, vec_ok);
+    const bool whole = fast_ok(*tile, M, N, K);
+    const bool edge = !whole && K > 0 && end_ok;
 
     int variant = req.variant;
     // With one K tile there is nothing to overlap ("Pipeline GPU Kernel",
@@ -494,28 +521,30 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const bool one_tile = ceil_div(K, cfg_bk(*tile)) < 2;
     if (variant == TDG_VARIANT_AUTO)
         variant = pipelined_default && !one_tile
-                      ? (fast || edge ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
+                      ? (whole || edge ? TDG_VARIANT_DIRECT_LDS : TDG_VARIANT_REG_PREFETCH)
                       : TDG_VARIANT_SINGLE;
     int stages = req.lds_stages;
     if (stages == 0)
         stages = variant == TDG_VARIANT_SINGLE ? 1
                  : variant == TDG_VARIANT_REG_PREFETCH ? 2
-                                                       : direct_stages(!fast);
+                                                       : direct_stages(!whole);
     if (variant == TDG_VARIANT_SINGLE && stages != 1) return TDG_ERR_UNSUPPORTED;
     if (variant == TDG_VARIANT_REG_PREFETCH && stages > 2) return TDG_ERR_UNSUPPORTED;
     if (variant == TDG_VARIANT_DIRECT_LDS && stages < 2) return TDG_ERR_UNSUPPORTED;
 
-    bool guard = !fast;
+    // The direct-to-LDS loop runs unchecked on whole tiles at any alignment;
+    // the register and sequential loops only when the rows are also aligned.
+    bool guard = variant == TDG_VARIANT_DIRECT_LDS ? !whole : !(whole && vec_ok);
     const KernelEntry *e = nullptr;
     if (!guard) {
         e = find_entry(*tile, stages, variant, false);
     } else if (variant == TDG_VARIANT_DIRECT_LDS) {
-        // The DMA needs valid, aligned sources for every 16-byte chunk
-        // ("Pipeline GPU Kernel", Common Pitfalls).  Ragged shapes whose rows
-        // are aligned whole chunks keep the copy in the DMA (bounds-checked
-        // form, at the asked ring depth if built, else the tile's preferred
-        // one, else two buffers); anything else runs the bounds-checked
-        // register-prefetch loop.
+        // The DMA needs a valid source for every 16-byte chunk ("Pipeline
+        // GPU Kernel", Common Pitfalls): ragged shapes keep the copy in the
+        // DMA's bounds-checked form (at the asked ring depth if built, else
+        // the tile's preferred one, else two buffers); a K of zero, or an
+        // operand whose last chunk would enter a page beyond it (not
+        // ends_in_page), runs the bounds-checked register-prefetch loop.
         if (edge) {
             e = find_entry(*tile, stages, variant, true);
             if (!e) {
@@ -562,10 +591,11 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
 
 // Recent resolutions, so that repeated calls on one shape skip the table
 // scans.  The key holds everything resolve() reads: the request, the shape,
-// the operands' alignment and the leading dimensions (which decide whether
-// the chosen kernel's 32-bit per-lane offsets reach every chunk).
+// the operands' alignment, whether their last chunks stay in their pages,
+// and the leading dimensions (which decide whether the chosen kernel's
+// 32-bit per-lane offsets reach every chunk).
 struct PlanKey {
-    int dtype, variant_req, bm, bn, bk, waves, stages, pipelined_default, vec_ok;
+    int dtype, variant_req, bm, bn, bk, waves, stages, pipelined_default, vec_ok, end_ok;
     int64_t M, N, K, lda, ldb;
     bool operator==(const PlanKey &o) const { return memcmp(this, &o, sizeof(PlanKey)) == 0; }
 };
@@ -593,6 +623,7 @@ int resolve_cached(int dtype, int64_t M, int64_t N, int64_t K, const void *A, in
     key.stages = req.lds_stages;
     key.pipelined_default = pipelined_default ? 1 : 0;
     key.vec_ok = aligned_operands(dtype, A, lda, B, ldb) ? 1 : 0;
+    key.end_ok = ends_in_page(dtype, M, N, K, A, lda, B, ldb) ? 1 : 0;
     key.M = M;
     key.N = N;
     key.K = K;
@@ -606,7 +637,7 @@ int resolve_cached(int dtype, int64_t M, int64_t N, int64_t K, const void *A, in
                 return slot.rc;
             }
     }
-    const int rc = resolve(dtype, M, N, K, A, lda, B, ldb, req, pipelined_default, out, nullptr,
+    const int rc = resolve(dtype, M, N, K, A, lda, B, ldb, key.end_ok != 0, req, pipelined_default, out, nullptr,
                            nullptr);
     std::lock_guard<std::mutex> lock(g_plan_mutex);
     PlanSlot &slot = g_plans[g_plan_next++ % 16];
@@ -850,11 +881,26 @@ int tdg_plan(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *out, tdg_pl
     memset(&req, 0, sizeof(req));
     if (out) req = *out;
     // Planning assumes dense operands (lda = K, ldb = N) at 16-byte aligned
-    // addresses; any stride or alignment the real call has is judged again
-    // when it runs.
+    // addresses whose last chunks stay in their pages; the real call's
+    // strides and addresses are judged again when it runs
+    // (tdg_plan_operands tells what they make of it).
     const void *aligned = (const void *)(uintptr_t)4096;
     const int64_t lda = K > 0 ? K : 1, ldb = N > 0 ? N : 1;
-    return resolve(dtype, M, N, K, aligned, lda, aligned, ldb, req, true, nullptr, out, info);
+    return resolve(dtype, M, N, K, aligned, lda, aligned, ldb, true, req, true, nullptr, out, info);
+}
+
+int tdg_plan_operands(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                      const void *B, int64_t ldb, tdg_config *out, tdg_plan_info *info) {
+    if (!dtype_ok(dtype) || !dims_ok(M, N, K)) return TDG_ERR_INVALID_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1)) return TDG_ERR_INVALID_ARG;
+    if ((M > 0 && K > 0 && !A) || (K > 0 && N > 0 && !B)) return TDG_ERR_INVALID_ARG;
+    const int es = elem_size(dtype);
+    if (!extent_ok(M, lda, es) || !extent_ok(K, ldb, es)) return TDG_ERR_INVALID_ARG;
+    tdg_config req;
+    memset(&req, 0, sizeof(req));
+    if (out) req = *out;
+    return resolve(dtype, M, N, K, A, lda, B, ldb, ends_in_page(dtype, M, N, K, A, lda, B, ldb), req, true,
+                   nullptr, out, info);
 }
 
 int tdg_predict_us(int dtype, int bm, int bn, int waves, int stages, int64_t M, int64_t N, int64_t K,

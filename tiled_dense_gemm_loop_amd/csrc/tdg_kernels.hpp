@@ -510,13 +510,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // inline assembly so that the compiler does not guard the other buffer's
     // LDS reads with a wait on these copies; completion is awaited
     // explicitly (vmcnt) before the barrier that publishes the tile.
-    // Bounds-checked DMA (GUARD, with the `checked` tag set): the operands'
-    // rows are 16-byte aligned, so every 16-byte chunk starts on a 16-byte
-    // boundary.  A chunk that starts outside its matrix (A row >= M, k >= K;
-    // B row k >= K, column >= N) is fetched from the zero block instead; one
-    // that starts inside is fetched whole, also when K or N ends inside it
-    // (it lies in one 4 KiB page with a byte of the matrix).  The source is
-    // then a per-lane 64-bit address.  B columns >= N and A rows >= M only
+    // Bounds-checked DMA (GUARD, with the `checked` tag set): chunks sit on a
+    // 16-byte grid from each row's first byte, at any alignment (the DMA
+    // reads 16 bytes from any byte address).  A chunk that starts outside its
+    // matrix (A row >= M, k >= K; B row k >= K, column >= N) is fetched from
+    // the zero block instead; one that starts inside is fetched whole, also
+    // when K or N ends inside it.  Its bytes past the row's end then belong
+    // to the next row, except at the end of the last row, where the host
+    // runs this loop only when the chunk holding the operand's last byte
+    // stays in that byte's 4 KiB page.  The source is then a per-lane 64-bit
+    // address.  B columns >= N and A rows >= M only
     // feed C elements that are never stored; k >= K must be zero, which the
     // zero block gives for whole chunks and clear_k_tail for the one A chunk
     // per row that K splits.  A bounds-checked kernel issues the plain form (wave-uniform
@@ -808,11 +811,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 if (w >= w_chk) issue_direct(off, w, checked_t{});
                 else issue_direct(off, w, unchecked_t{});
             };
-            // A K that splits a 16-byte chunk (rows still 16-byte aligned):
-            // the last K tile's straddling chunk of every A row is fetched
-            // whole -- a 16-byte aligned chunk lies inside one 4 KiB page,
-            // and its first byte is inside A -- so its bytes at k >= K hold
-            // whatever follows in memory.  Once that tile has landed and
+            // A K that splits a 16-byte chunk: the last K tile's straddling
+            // chunk of every A row is fetched whole (see the bounds-checked
+            // DMA above), so its bytes at k >= K hold whatever follows in
+            // memory.  Once that tile has landed and
             // been published, each row's chunk is cleared from byte
             // (K - k0) * sizeof(T) % 16 on, and a second barrier publishes
             // the cleared tile before any fragment is read.  (B needs no
