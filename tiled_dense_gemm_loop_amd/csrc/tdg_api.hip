@@ -147,8 +147,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // A shape of whole tiles: M, N and K multiples of the tile, so every row
 // of a K tile is whole 16-byte chunks and no chunk runs past its row.  The
 // unchecked direct-to-LDS loop serves it at any alignment: the LDS DMA reads
-// its 16 bytes from any byte address (checked on the GPU for every offset
-// 0..15).  The unchecked register and sequential loops load through 16-byte
+// its 16 bytes from any byte address (the parity tests run it at every
+// byte offset of a chunk).  The unchecked register and sequential loops load through 16-byte
 // vector types and also need 16-byte aligned rows (aligned_operands).
 bool fast_ok(const KernelEntry &e, int64_t M, int64_t N, int64_t K) {
     const int bk = cfg_bk(e);
