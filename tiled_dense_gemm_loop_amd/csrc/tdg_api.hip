@@ -413,12 +413,29 @@ struct Choice {
     int stages;               // ring depth for the direct-to-LDS loop; 0 = none measured
 };
 
+// The table's times are for 16-byte aligned rows.  With rows off that grid
+// a 128-byte K-tile row of A spans two 128-byte lines instead of one, and
+// the copy of every tile costs more, the more so the more bytes a
+// configuration copies per compute unit and the shallower its ring.
+// Measured at 4096^3 (rows 2 bytes off, every direct-to-LDS configuration):
+// about 7 (FP16) to 10 (INT8) us per MB of L2 -> LDS traffic per compute
+// unit with two buffers, and about three quarters of that with three or
+// four (256 x 128: 45 against 33 us; 128 x 128: 59 against 46 us, FP16).
+constexpr double kMisalignedUsPerMB = 8.0;
+
+double misaligned_penalty_us(int64_t grid, int bm, int bn, int stages, int64_t K, int es) {
+    const double mb_per_cu = (double)grid * (bm + bn) * (double)K * es / kNumCU / 1e6;
+    return kMisalignedUsPerMB * mb_per_cu * (stages > 2 ? 0.75 : 1.0);
+}
+
 // Tile shape, waves and ring depth for a product: the measured configuration
 // with the least predicted time (a near tie, within 3%, goes to the earlier
-// row).  Requests outside the measured table (other K tiles, or a tile,
+// row), with the copy's extra cost added when the rows are not 16-byte
+// aligned.  Requests outside the measured table (other K tiles, or a tile,
 // wave count or ring depth no row has) fall back to the largest tile that
 // gives every compute unit a workgroup, or the one giving the most.
-Choice choose_config(int dtype, int64_t M, int64_t N, int64_t K, const tdg_config &req) {
+Choice choose_config(int dtype, int64_t M, int64_t N, int64_t K, const tdg_config &req,
+                     bool rows_aligned = true) {
     const PerfRow *best = nullptr;
     const KernelEntry *best_tile = nullptr;
     double best_t = 0.0;
@@ -436,7 +453,8 @@ Choice choose_config(int dtype, int64_t M, int64_t N, int64_t K, const tdg_confi
             tdg_plan_info fig;
             tile_figures(dtype, r.bm, r.bn, 128 / es, r.waves, r.stages, TDG_VARIANT_DIRECT_LDS, M, N,
                          K, &fig);
-            const double t_us = predict_us(r, fig.wg_per_cu, fig.grid, K);
+            double t_us = predict_us(r, fig.wg_per_cu, fig.grid, K);
+            if (!rows_aligned) t_us += misaligned_penalty_us(fig.grid, r.bm, r.bn, r.stages, K, es);
             if (!best || t_us < best_t * 0.97) {
                 best = &r;
                 best_tile = t;
@@ -499,7 +517,8 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     tdg_config req = req_in;
     if (req.variant < 0 || req.variant > TDG_VARIANT_DIRECT_LDS) return TDG_ERR_INVALID_ARG;
     if (req.lds_stages < 0 || req.lds_stages > 8) return TDG_ERR_UNSUPPORTED;
-    const Choice choice = choose_config(dtype, M, N, K, req);
+    const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
+    const Choice choice = choose_config(dtype, M, N, K, req, vec_ok);
     const KernelEntry *tile = choice.tile;
     if (!tile) return TDG_ERR_UNSUPPORTED;
     // Ring depth of the direct-to-LDS loop when the caller leaves it open:
@@ -510,7 +529,6 @@ int resolve(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
             return choice.stages;
         return 2;
     };
-    const bool vec_ok = aligned_operands(dtype, A, lda, B, ldb);
     const bool whole = fast_ok(*tile, M, N, K);
     const bool edge = !whole && K > 0 && end_ok;
 
