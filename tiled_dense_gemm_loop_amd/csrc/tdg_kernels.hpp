@@ -789,7 +789,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
             // every wait is AHEAD - 1 and the wait count is a constant.
             constexpr int AHEAD = STAGES - 1;
             constexpr int IPT = G::CA + G::CB;  // DMA instructions per wave per tile
-            static_assert((AHEAD - 1) * IPT <= 63, "vmcnt holds at most 63");
+            static_assert(AHEAD * IPT <= 63, "vmcnt holds at most 63");
             auto stage_off = [&](int t) { return (uint32_t)((t % STAGES) * G::STAGE_BYTES); };
             auto src_tile = [&](int t) { return t < nt ? t : nt - 1; };
             // Walk positions from `w_chk` on take the bounds-checked DMA: all
@@ -851,13 +851,18 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 __syncthreads();
             };
             // Prologue: tiles 0 .. AHEAD-1 in flight, tile 0 published, tile
-            // AHEAD issued into the still unused last buffer.
+            // AHEAD issued into the still unused last buffer.  The unchecked
+            // loop issues tile AHEAD before the wait (every buffer is free at
+            // the start), so that it loads during tile 0's wait as well as
+            // its compute; the bounds-checked loop, which has no registers
+            // to spare for it, after the barrier.
+            constexpr int EARLY = GUARD ? 0 : 1;
 #pragma unroll
-            for (int p = 0; p < AHEAD; p++) issue_pos(stage_off(p), src_tile(p));
-            wait_vmcnt<(AHEAD - 1) * IPT>();
+            for (int p = 0; p < AHEAD + EARLY; p++) issue_pos(stage_off(p), src_tile(p));
+            wait_vmcnt<(AHEAD - 1 + EARLY) * IPT>();
             __syncthreads();
             clear_k_tail(0);
-            issue_pos(stage_off(AHEAD), src_tile(AHEAD));
+            if (!EARLY) issue_pos(stage_off(AHEAD), src_tile(AHEAD));
             read_first(buf(0));
             // Main loop and epilogue (from tile nt - AHEAD on, the issued
             // loads are the harmless repeats).  The DMA interleaved with tile
