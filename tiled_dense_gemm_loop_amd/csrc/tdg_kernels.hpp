@@ -384,27 +384,44 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // base plus a constant (folded into the instruction's offset field).
     const uint32_t b_roff32 = (uint32_t)(G::A_BYTES + ((lane >> 5) * 4) * G::B_ROWB +
                                          (wn * G::WTN + (lane & 31)) * G::ES);
-    uint32_t b_roff[G::TRB ? G::KSTEPS : 1][G::TRB ? G::B_RD : 1][G::NI];
+    // Transposed B reads (FP16, INT8): the swizzle of a k-row repeats every
+    // TR_ROWS rows, and K steps and the reads within a step advance k by
+    // multiples of TR_ROWS, so every read of column block ni is one per-lane
+    // offset (step 0, read 0) plus a compile-time constant that goes into the
+    // instruction's offset field.  With two or more column blocks per wave
+    // that saves registers: one per block instead of one per (step, read,
+    // block), 12 fewer in the 8-wave INT8 256 x 256 kernel, which gave the
+    // bounds-checked kernels room for the 3-step read distance.  With one
+    // block (the 64 x 64 tile) the per-step offsets are kept: folded, the
+    // skinny product ran 1.3% slower (and FP16 1024^3 2% faster).
+    constexpr int B_KS = 32 / G::ES;   // k per MFMA step
+    constexpr int B_KR = G::TR_ROWS;   // k per transposed read
+    static_assert(!G::TRB || (B_KS % G::TR_ROWS == 0 && (B_KS / 2) % G::TR_ROWS == 0),
+                  "B swizzle must repeat across K steps");
+    constexpr bool B_FOLD = G::NI >= 2;
+    constexpr int B_S = G::TRB && !B_FOLD ? G::KSTEPS : 1, B_H = G::TRB && !B_FOLD ? G::B_RD : 1;
+    uint32_t b_roff[B_S][B_H][G::TRB ? G::NI : 1];
     if constexpr (G::TRB) {
-        constexpr int KS = 32 / G::ES;       // k per MFMA step
-        constexpr int KH = KS / 2;           // k per lane half (lane / 32)
-        constexpr int KR = G::TR_ROWS;       // k per transposed read
 #pragma unroll
-        for (int s = 0; s < G::KSTEPS; s++)
+        for (int s = 0; s < B_S; s++)
 #pragma unroll
-            for (int h = 0; h < G::B_RD; h++) {
-                // k-row group h of the lane's half
-                const int k = s * KS + (lane >> 5) * KH + h * KR + (lane & 15) / G::LPR;
+            for (int h = 0; h < B_H; h++) {
+                // k-row group h of the lane's half (lane / 32) of step s
+                const int k = s * B_KS + (lane >> 5) * (B_KS / 2) + h * B_KR + (lane & 15) / G::LPR;
 #pragma unroll
                 for (int ni = 0; ni < G::NI; ni++) {
-                    const int n = wn * G::WTN + ni * 32 + ((lane >> 4) & 1) * 16 +
-                                  (lane % G::LPR) * G::EPL;
+                    const int n = wn * G::WTN + ni * 32 + ((lane >> 4) & 1) * 16 + (lane % G::LPR) * G::EPL;
                     const int byte = n * G::ES;
                     b_roff[s][h][ni] = (uint32_t)(G::A_BYTES + k * G::B_ROWB +
                                                   (((byte >> 4) ^ G::swz_b(k)) << 4) + (byte & 15));
                 }
             }
     }
+    // LDS offset of read h of K step s of column block ni.
+    auto b_off = [&](int s, int h, int ni) -> uint32_t {
+        if constexpr (B_FOLD) return b_roff[0][0][ni] + (uint32_t)((s * B_KS + h * B_KR) * G::B_ROWB);
+        else return b_roff[s][h][ni];
+    };
 
     acc_t acc[G::MI][G::NI];
 #pragma unroll
@@ -592,20 +609,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // costs no exposed LDS latency either.
     static_assert(G::KSTEPS % 2 == 0, "fragment set parity must repeat per tile");
     // Fragment read distance: when a tile has 4 K steps, the direct-to-LDS
-    // loop keeps one register set per step and reads 3 steps ahead (2 in its
-    // bounds-checked form, whose address work leaves no registers for the
-    // fourth live set), else 1 (two sets); the register-prefetch loop has no
-    // room for more sets beside its staging.  Reading 3 steps ahead put the
-    // tile boundary, with its wait and barrier, one step earlier, and together
-    // with the copies spread over two steps (below) made the 256 x 256
-    // tiles about 1.5% faster (FP16 and INT8 4096^3).
-    constexpr int FD = (VAR == VAR_DIRECT && G::KSTEPS == 4) ? (GUARD ? 2 : 3) : 1;
+    // loop keeps one register set per step and reads 3 steps ahead, else 1
+    // (two sets); the register-prefetch loop has no room for more sets beside
+    // its staging.  Reading 3 steps ahead put the tile boundary, with its
+    // wait and barrier, one step earlier, and together with the copies spread
+    // over two steps (below) made the 256 x 256 tiles about 1.5% faster (FP16
+    // and INT8 4096^3).
+    constexpr int FD = (VAR == VAR_DIRECT && G::KSTEPS == 4) ? 3 : 1;
     constexpr int NSETS = FD == 1 ? 2 : G::KSTEPS;
     static_assert(FD == 1 || NSETS == G::KSTEPS, "set index must equal the step index");
     u32x4 fa[NSETS][G::MI], fb[NSETS][G::NI];
     auto read_bfrag = [&](const unsigned char *st, int s, int ni) -> u32x4 {
         if constexpr (G::TRB) {
-            return MM::read_b(st + b_roff[s][0][ni], st + b_roff[s][1][ni]);
+            return MM::read_b(st + b_off(s, 0, ni), st + b_off(s, 1, ni));
         } else {
             // rows k = 8 s + 4 (l / 32) + h, h = 0..3; column block ni
             const unsigned char *p = st + b_roff32 + (s * 8) * G::B_ROWB + ni * 32 * G::ES;
@@ -695,12 +711,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
     // interior tiles; the bounds-checked form keeps the drain at the
     // boundary, where its byte fix-ups cost less than between the MFMAs.
     // The copies of a later tile go out over SPREAD steps from the boundary
-    // on: two in the unchecked direct-to-LDS loop with a read distance of 2
-    // or more, which halves the vector-memory instructions per step; one in
-    // the bounds-checked form, whose checked copies cost more there (FP16
-    // 4000^3: 5% slower over two steps).  Every copy of the tile is issued
-    // before the next boundary, so the vmcnt counts do not change.
-    constexpr int SPREAD = VAR == VAR_DIRECT && !GUARD && FD >= 2 ? 2 : 1;
+    // on: two in the direct-to-LDS loop with a read distance of 2 or more,
+    // which halves the vector-memory instructions per step.  Every copy of
+    // the tile is issued before the next boundary, so the vmcnt counts do
+    // not change.
+    constexpr int SPREAD = VAR == VAR_DIRECT && FD >= 2 ? 2 : 1;
     constexpr int ND_ALL = G::CA + G::CB;
     int dma_tile = 0;
     uint32_t dma_off = 0;
@@ -850,19 +865,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) tdg_gemm_kernel(GemmArgs args
                 }
                 __syncthreads();
             };
-            // Prologue: tiles 0 .. AHEAD-1 in flight, tile 0 published, tile
-            // AHEAD issued into the still unused last buffer.  The unchecked
-            // loop issues tile AHEAD before the wait (every buffer is free at
-            // the start), so that it loads during tile 0's wait as well as
-            // its compute; the bounds-checked loop, which has no registers
-            // to spare for it, after the barrier.
-            constexpr int EARLY = GUARD ? 0 : 1;
+            // Prologue: tiles 0 .. AHEAD issued into the STAGES buffers, all
+            // free at the start, then tile 0 awaited (the AHEAD younger tiles
+            // stay in flight) and published: tile AHEAD loads during tile 0's
+            // wait as well as its compute.
 #pragma unroll
-            for (int p = 0; p < AHEAD + EARLY; p++) issue_pos(stage_off(p), src_tile(p));
-            wait_vmcnt<(AHEAD - 1 + EARLY) * IPT>();
+            for (int p = 0; p <= AHEAD; p++) issue_pos(stage_off(p), src_tile(p));
+            wait_vmcnt<AHEAD * IPT>();
             __syncthreads();
             clear_k_tail(0);
-            if (!EARLY) issue_pos(stage_off(AHEAD), src_tile(AHEAD));
             read_first(buf(0));
             // Main loop and epilogue (from tile nt - AHEAD on, the issued
             // loads are the harmless repeats).  The DMA interleaved with tile
