@@ -292,8 +292,9 @@ def transpose_ladder(tdg):
 def measured_ceilings(tdg, ladder):
     """Second denominators: the MFMA rate the chip sustains with no memory
     traffic (tdg_mfma_probe, ~20 ms per launch, 5 launches after 2, so the
-    power controller settles) and the bandwidth of the library's copy on a
-    matrix far larger than the last-level cache."""
+    power controller settles), the LDS read rate per CU of the fragment
+    reads' instruction forms (tdg_lds_probe), and the bandwidth of the
+    library's copy on a matrix far larger than the last-level cache."""
     import torch
     out = {}
     sink = torch.empty(tdg.tdg_mfma_probe_sink_floats(), dtype=torch.float32, device="cuda")
@@ -302,6 +303,8 @@ def measured_ceilings(tdg, ladder):
                              (tdg.TDG_DTYPE_F32F32, "mfma_f32_tflops", 40000)):
         ms = time_launches(lambda: tdg.tdg_mfma_probe(code, iters, sink), 5, 2)
         out[key] = round(tdg.tdg_mfma_probe_ops(code, iters) / (ms * 1e-3) / 1e12, 1)
+    for name, mode in tdg.LDS_PROBE_MODES.items():
+        out["lds_%s_bytes_per_clk" % name] = round(tdg.tdg_lds_probe(mode, 4096), 1)
     if ladder and "16384x16384" in ladder:
         out["copy_gbs"] = ladder["16384x16384"]["copy"]["gbs"]
     print("# measured ceilings %s" % json.dumps(out), file=sys.stderr, flush=True)

@@ -393,6 +393,20 @@ int tdg_mfma_probe(int dtype, int64_t iters, float *sink, void *stream);
 int64_t tdg_mfma_probe_ops(int dtype, int64_t iters);
 int64_t tdg_mfma_probe_sink_floats(void);
 
+/* The measured LDS read rate ("Analyze Kernel Bottleneck", Step 2: compare
+ * with what the hardware delivers): one 8-wave workgroup per compute unit
+ * reads its 64 KiB of LDS `iters` x 8 times per thread, without bank
+ * conflicts, with mode 0 = 16-byte reads (ds_read_b128, the GEMM's A
+ * fragments), 1 = transposing 8-byte reads (ds_read_b64_tr_b16, its B
+ * fragments), 2 = plain 8-byte reads (ds_read_b64).  `out` is a device
+ * array of 512 uint32: out[w] receives workgroup w's shader cycles
+ * (s_memtime), out[256 + w] a value of its reads.  tdg_lds_probe_bytes
+ * gives the bytes one workgroup reads (-1 for a bad mode or iters), so
+ * bytes / cycles is the per-CU rate per clock.  TDG_ERR_INVALID_ARG for a
+ * bad mode, negative iters or NULL out; TDG_ERR_NO_DEVICE off gfx950. */
+int tdg_lds_probe(int mode, int64_t iters, uint32_t *out, void *stream);
+int64_t tdg_lds_probe_bytes(int mode, int64_t iters);
+
 #ifdef __cplusplus
 }
 #endif

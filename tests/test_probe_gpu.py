@@ -1,5 +1,6 @@
-"""The measured-ceiling probe runs and reports the work it does; the
-runtime's view of every built kernel matches the planner's LDS arithmetic."""
+"""The measured-ceiling probes (MFMA-only, LDS read rate) run and report the
+work they do; the runtime's view of every built kernel matches the
+planner's LDS arithmetic."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -19,6 +20,28 @@ def test_mfma_probe_runs_and_counts():
         assert t.tdg_mfma_probe_ops(code, 8) == 2 * 32 * 32 * k * 8 * 8 * 2048
     with pytest.raises(t.TdgError):
         t.tdg_mfma_probe(t.TDG_DTYPE_F16F32, 6)   # not a multiple of 4
+
+
+def test_lds_probe_rates():
+    """The LDS read-rate probe runs in every mode and counts its bytes; the
+    rates it measures are what the micro-kernel's schedule assumes: 16-byte
+    reads move at least 1.5 times the bytes per clock of the 8-byte
+    (transposing or plain) reads, and no mode exceeds the 256 bytes per
+    clock that 64 banks of 4 bytes deliver."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import tiled_dense_gemm_loop_amd as t
+    t.load_library()
+    rates = {}
+    for name, mode in t.LDS_PROBE_MODES.items():
+        assert t.tdg_lds_probe_bytes(mode, 100) == 100 * 8 * 512 * (16 if mode == 0 else 8)
+        rates[name] = t.tdg_lds_probe(mode, 2048)
+        assert 0 < rates[name] <= 256 * 1.02, rates
+    assert rates["b128"] >= 1.5 * rates["b64_tr_b16"], rates
+    assert rates["b128"] >= 1.5 * rates["b64"], rates
+    with pytest.raises(t.TdgError):
+        t.tdg_lds_probe(3, 10)
 
 
 def test_config_resources_match_the_lds_budget():

@@ -49,7 +49,8 @@ EXPORTED = (
     "gemm_f16f32_ex", "gemm_i8i32_ex", "gemm_f32f32", "gemm_f32f32_pipelined", "gemm_f32f32_ex",
     "tdg_plan", "tdg_plan_operands", "tdg_tile_figures", "tdg_config_count",
     "tdg_config_at", "tdg_status_string", "tdg_set_debug_flags", "tdg_copy_f32", "tdg_transpose_f32",
-    "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats",
+    "tdg_mfma_probe", "tdg_mfma_probe_ops", "tdg_mfma_probe_sink_floats", "tdg_lds_probe",
+    "tdg_lds_probe_bytes",
     "gemm_f16f32_splitk", "gemm_i8i32_splitk", "gemm_f32f32_splitk", "tdg_splitk_plan",
     "tdg_config_resources", "gemm_splitk_noalloc", "tdg_predict_us",
 )
@@ -161,6 +162,10 @@ def load_library(path: str = LIB_PATH):
     lib.tdg_mfma_probe_ops.restype = i64
     lib.tdg_mfma_probe_sink_floats.argtypes = []
     lib.tdg_mfma_probe_sink_floats.restype = i64
+    lib.tdg_lds_probe.argtypes = [c_int, i64, vp, vp]
+    lib.tdg_lds_probe.restype = c_int
+    lib.tdg_lds_probe_bytes.argtypes = [c_int, i64]
+    lib.tdg_lds_probe_bytes.restype = i64
     _lib = lib
     return lib
 
@@ -524,6 +529,33 @@ def tdg_mfma_probe_ops(dtype: int, iters: int) -> int:
 
 def tdg_mfma_probe_sink_floats() -> int:
     return load_library().tdg_mfma_probe_sink_floats()
+
+
+LDS_PROBE_MODES = {"b128": 0, "b64_tr_b16": 1, "b64": 2}
+
+
+def tdg_lds_probe_bytes(mode: int, iters: int) -> int:
+    """Bytes one workgroup of tdg_lds_probe reads."""
+    return load_library().tdg_lds_probe_bytes(mode, iters)
+
+
+def tdg_lds_probe(mode: int, iters: int = 4096, out=None) -> float:
+    """Run the LDS read-rate kernel on the current stream and wait for it;
+    returns the mean bytes per shader clock per compute unit."""
+    torch = _torch()
+    if out is None:
+        out = torch.zeros(512, dtype=torch.int32, device="cuda")
+    if out.dtype != torch.int32 or out.numel() < 512 or not out.is_cuda:
+        raise ValueError("out must be a device int32 tensor of at least 512 elements")
+    lib = load_library()
+    with torch.cuda.device(out.device):
+        stream = torch.cuda.current_stream(out.device).cuda_stream
+        rc = lib.tdg_lds_probe(mode, iters, out.data_ptr(), stream)
+    if rc != TDG_OK:
+        raise TdgError(rc, "tdg_lds_probe")
+    torch.cuda.synchronize(out.device)
+    cycles = out[:256].cpu().long() & 0xFFFFFFFF
+    return tdg_lds_probe_bytes(mode, iters) / float(cycles.double().mean())
 
 
 def tdg_mfma_probe(dtype: int, iters: int, sink=None):

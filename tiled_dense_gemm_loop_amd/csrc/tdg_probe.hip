@@ -112,9 +112,80 @@ __global__ void __launch_bounds__(PROBE_THREADS) k_mfma_probe(int64_t iters, flo
     sink[lane] = total;  // keeps the chains live
 }
 
+// LDS read rate.  One workgroup of 8 waves per CU (2 per SIMD, like the
+// 8-wave GEMM tile) reads its 64 KiB LDS buffer in a loop: 16-byte reads
+// (ds_read_b128, the A fragments), transposing 8-byte reads
+// (ds_read_b64_tr_b16, the B fragments) or plain 8-byte reads
+// (ds_read_b64).  Lane l reads 16 (or 8) bytes at l * 16 within a 1 KiB
+// row, and waves and reads move over the 64 rows, so no two lanes of a read
+// share a bank.  The loads are volatile (or intrinsics the compiler does not
+// merge), so every one issues.  Each workgroup writes its shader cycles
+// (s_memtime) to out[blockIdx], and a value of its reads to
+// out[PROBE_CUS + blockIdx], which keeps them live.
+constexpr int LDS_PROBE_THREADS = 512;
+constexpr int LDS_PROBE_BYTES = 65536;
+constexpr int LDS_PROBE_UNROLL = 8;
+
+template <int MODE>
+__global__ void __launch_bounds__(LDS_PROBE_THREADS) k_lds_probe(int64_t iters, uint32_t *out) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_PROBE_BYTES];
+    typedef __attribute__((address_space(3))) unsigned char lds_byte;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid * 16; i < LDS_PROBE_BYTES; i += LDS_PROBE_THREADS * 16)
+        *(u32x4 *)(lds + i) = u32x4{(uint32_t)i, 1u, 2u, 3u};
+    __syncthreads();
+    lds_byte *base = (lds_byte *)lds + lane * 16;
+    uint32_t acc = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int64_t it = 0; it < iters; it++) {
+#pragma unroll
+        for (int j = 0; j < LDS_PROBE_UNROLL; j++) {
+            const int row = (int)(((it * LDS_PROBE_UNROLL + j) * 8 + wave) & 63);
+            lds_byte *p = base + row * 1024;
+            if constexpr (MODE == 0) {
+                const u32x4 v = *(volatile const __attribute__((address_space(3))) u32x4 *)p;
+                acc ^= v[0] ^ v[3];
+            } else if constexpr (MODE == 1) {
+                const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)p);
+                acc ^= (uint32_t)(uint16_t)v[0] ^ (uint32_t)(uint16_t)v[3];
+            } else {
+                const i16x4 v = *(volatile const __attribute__((address_space(3))) i16x4 *)p;
+                acc ^= (uint32_t)(uint16_t)v[0] ^ (uint32_t)(uint16_t)v[3];
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    if (tid == 0) {
+        out[blockIdx.x] = (uint32_t)(t1 - t0);
+        out[PROBE_CUS + blockIdx.x] = acc;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t tdg_lds_probe_bytes(int mode, int64_t iters) {
+    if (mode < 0 || mode > 2 || iters < 0) return -1;
+    return iters * LDS_PROBE_UNROLL * LDS_PROBE_THREADS * (mode == 0 ? 16 : 8);
+}
+
+int tdg_lds_probe(int mode, int64_t iters, uint32_t *out, void *stream) {
+    if (mode < 0 || mode > 2 || iters < 0 || !out) return TDG_ERR_INVALID_ARG;
+    const int dev = tdg::device_check();
+    if (dev != TDG_OK) return dev;
+    void *kargs[] = {&iters, &out};
+    const void *fn = mode == 0 ? (const void *)&k_lds_probe<0>
+                     : mode == 1 ? (const void *)&k_lds_probe<1>
+                                 : (const void *)&k_lds_probe<2>;
+    if (hipLaunchKernel(fn, dim3(PROBE_CUS), dim3(LDS_PROBE_THREADS), kargs, 0, (hipStream_t)stream) !=
+        hipSuccess)
+        return TDG_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess) return TDG_ERR_LAUNCH;
+    return TDG_OK;
+}
 
 static bool probe_dtype(int dtype) {
     return dtype == TDG_DTYPE_F16F32 || dtype == TDG_DTYPE_I8I32 || dtype == TDG_DTYPE_F32F32;
