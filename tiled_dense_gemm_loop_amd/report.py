@@ -264,6 +264,15 @@ def report(wl: str, detail: dict, profiles: str) -> str:
                 prof.get("bank_conflict", 0), prof["lds_active"], prof.get("bank_conflict", 0) / prof["lds_active"]))
         if prof.get("mfma_util") is not None:
             L.append("- MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over the active cycles): %.1f%%." % (100 * prof["mfma_util"]))
+        b128 = ceilings.get("lds_b128_bytes_per_clk")
+        if b128 and prof.get("lds") and prof.get("grbm"):
+            per_instr = 64 * 16 / b128     # cycles per wave-wide LDS read, from the probe
+            busy = prof["lds"] / NUM_CU * per_instr / (prof["grbm"] / 8.0)
+            L.append("- LDS issue: the probe (`tdg_lds_probe`) measures %.0f bytes per clock per CU for 16-byte "
+                     "reads and %.0f for 8-byte transposing ones, i.e. one wave-wide read every %.1f cycles; the "
+                     "%.0f LDS instructions per CU keep the LDS busy %.0f%% of the active cycles, before the "
+                     "DMA's writes." % (b128, ceilings.get("lds_b64_tr_b16_bytes_per_clk", float("nan")), per_instr,
+                                        prof["lds"] / NUM_CU, 100 * busy))
     # LDS cliff
     lds = (res or {}).get("lds_bytes") or plan["lds_bytes"]
     per_cu = LDS_PER_CU // max(1, lds)
