@@ -598,34 +598,63 @@ def test_tails_at_every_page_offset(lib, dtype):
 @pytest.mark.parametrize("dtype", [F16, I8, F32])
 def test_random_shapes_strides_and_configs(lib, dtype):
     """A seeded sweep over the space the other tests sample by hand: random
-    M, N, K (1..700), leading dimensions padded by 0..20 elements, base
-    offsets of 0..3 elements for A, B and C, and for each case the planner's
-    choice plus a random built configuration (tile, waves, loop form,
-    stages).  Every result against the oracle; C's padding untouched."""
+    M, N, K (1..900, a third of them within 3 of a tile multiple), leading
+    dimensions padded by 0..40 elements and base offsets of 0..15 elements
+    for A, B and C (every byte offset of a 16-byte chunk for INT8, every
+    element offset for FP16 and FP32).  Each case runs the planner's choice,
+    the sequential loop, two random built configurations (tile, waves, loop
+    form, stages) and split K, a third of the launches with the LDS poisoned
+    between tiles.  Every result against the oracle, computed once per case;
+    C's padding untouched."""
     import random
     import torch
     rng = random.Random({F16: 11, I8: 12, F32: 13}[dtype])
     code = CODE[dtype]
     configs = [lib.tdg_config_at(code, i) for i in range(lib.tdg_config_count(code))]
     out_t = torch.int32 if dtype == I8 else torch.float32
-    for case in range(24):
-        M, N, K = rng.randint(1, 700), rng.randint(1, 700), rng.randint(1, 700)
-        pa, pb, pc = rng.randint(0, 20), rng.randint(0, 20), rng.randint(0, 20)
-        oa, ob, oc = rng.randint(0, 3), rng.randint(0, 3), rng.randint(0, 3)
-        bigA, bigB = _operands(dtype, M, N + pb + ob, K + pa + oa, seed=1000 + case)
-        bigB = bigB[:K, :]                   # K rows, ldb = N + pb + ob
-        A, B = bigA[:, oa:oa + K], bigB[:, ob:ob + N]
-        dBigA, dBigB = to_device(bigA), to_device(bigB)
-        dA, dB = dBigA[:, oa:oa + K], dBigB[:, ob:ob + N]
-        for cfg in (None, rng.choice(configs)):
-            bigC = torch.full((M, N + pc + oc), -7, dtype=out_t, device="cuda")
-            C = bigC[:, oc:oc + N]
-            if cfg is None:
-                gemm(lib, dtype, "pipelined", dA, dB, C)
+    split = {F16: lib.gemm_f16f32_splitk, I8: lib.gemm_i8i32_splitk, F32: lib.gemm_f32f32_splitk}[dtype]
+    prev = lib.tdg_set_debug_flags(0)
+    try:
+        for case in range(40):
+            if rng.random() < 0.3:
+                M, N, K = (max(1, rng.choice((64, 128, 256, 512, 768)) + rng.randint(-3, 3))
+                           for _ in range(3))
             else:
-                gemm(lib, dtype, "ex", dA, dB, C, cfg=cfg)
-            _check(dtype, C, A, B)
-            assert torch.all(bigC[:, :oc] == -7) and torch.all(bigC[:, oc + N:] == -7), (case, cfg)
+                M, N, K = rng.randint(1, 900), rng.randint(1, 900), rng.randint(1, 900)
+            pa, pb, pc = rng.randint(0, 40), rng.randint(0, 40), rng.randint(0, 40)
+            oa, ob, oc = rng.randint(0, 15), rng.randint(0, 15), rng.randint(0, 15)
+            bigA, bigB = _operands(dtype, M, N + pb + ob, K + pa + oa, seed=1000 + case)
+            bigB = bigB[:K, :]                   # K rows, ldb = N + pb + ob
+            A, B = bigA[:, oa:oa + K], bigB[:, ob:ob + N]
+            dBigA, dBigB = to_device(bigA), to_device(bigB)
+            dA, dB = dBigA[:, oa:oa + K], dBigB[:, ob:ob + N]
+            if dtype == I8:
+                ref, S = oracle.gemm_i8(A, B), None
+            else:
+                ref, S = (oracle.gemm_f32 if dtype == F32 else oracle.gemm_f16)(A, B)
+            runs = [("pipelined", None), ("single", None), ("ex", rng.choice(configs)),
+                    ("ex", rng.choice(configs)), ("splitk", rng.choice((0, 2, 3, 5)))]
+            for kind, arg in runs:
+                poison = rng.random() < 0.3
+                lib.tdg_set_debug_flags(lib.TDG_DEBUG_POISON_LDS if poison else 0)
+                what = (case, M, N, K, pa, pb, pc, oa, ob, oc, kind, arg, poison)
+                bigC = torch.full((M, N + pc + oc), -7, dtype=out_t, device="cuda")
+                C = bigC[:, oc:oc + N]
+                if kind == "splitk":
+                    split(dA, dB, C, parts=arg)
+                elif kind == "ex":
+                    gemm(lib, dtype, "ex", dA, dB, C, cfg=arg)
+                else:
+                    gemm(lib, dtype, kind, dA, dB, C)
+                got = C.cpu().numpy()
+                if dtype == I8:
+                    bad = np.argwhere(got.astype(np.int64) != ref)
+                else:
+                    bad = np.argwhere(np.abs(got.astype(np.float64) - ref) > 1e-4 * S)
+                assert bad.size == 0, (what, len(bad), tuple(bad[0]))
+                assert torch.all(bigC[:, :oc] == -7) and torch.all(bigC[:, oc + N:] == -7), what
+    finally:
+        lib.tdg_set_debug_flags(prev)
 
 
 @pytest.mark.parametrize("dtype", [F16, I8, F32])
