@@ -21,8 +21,9 @@
  *   - the _pipelined entry points run the prologue / main loop / epilogue
  *     form in which the global load of tile t+1 is in flight while the matrix
  *     cores compute on tile t, with two LDS buffers ("Pipeline GPU Kernel",
- *     Step 3 and Step 4).  The variant (register prefetch or direct
- *     global-to-LDS) is chosen per shape by tdg_plan.
+ *     Step 3 and Step 4) or a deeper ring of them.  The variant (register
+ *     prefetch or direct global-to-LDS) and the ring depth are chosen per
+ *     shape by tdg_plan.
  *
  * Pointers A, B, C are DEVICE pointers owned by the caller; the library never
  * allocates, frees or synchronises.  `stream` is a hipStream_t (NULL = the
@@ -164,10 +165,12 @@ int gemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
 /* Sequential (single-buffer) baseline, INT8 -> INT32. */
 int gemm_i8i32(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
-/* Software-pipelined, double-buffered K loop, FP16 -> FP32. */
+/* Software-pipelined K loop over double-buffered (or deeper) LDS tiles,
+ * FP16 -> FP32. */
 int gemm_f16f32_pipelined(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                           const uint16_t *B, int64_t ldb, float *C, int64_t ldc, void *stream);
-/* Software-pipelined, double-buffered K loop, INT8 -> INT32. */
+/* Software-pipelined K loop over double-buffered (or deeper) LDS tiles,
+ * INT8 -> INT32. */
 int gemm_i8i32_pipelined(int64_t M, int64_t N, int64_t K, const int8_t *A, int64_t lda,
                          const int8_t *B, int64_t ldb, int32_t *C, int64_t ldc, void *stream);
 /* Sequential baseline and pipelined loop, FP32 -> FP32. */
