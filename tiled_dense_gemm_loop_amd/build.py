@@ -9,7 +9,6 @@ from __future__ import annotations
 
 import os
 import subprocess
-import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -17,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libtdgemm.so")
+OBJ_DIR = os.path.join(PKG, "_build")  # object files of the last build
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
@@ -48,16 +48,18 @@ def _compile(unit, outdir):
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source and link libtdgemm.so next to this file."""
-    with tempfile.TemporaryDirectory(prefix="tdg_build_") as tmp:
-        with ThreadPoolExecutor(max_workers=len(UNITS)) as pool:
-            objs = list(pool.map(lambda u: _compile(u, tmp), UNITS))
-        tmp_lib = LIB_PATH + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-        os.replace(tmp_lib, LIB_PATH)
+    """Compile every HIP source and link libtdgemm.so next to this file.  The
+    objects stay in OBJ_DIR, where the host-code sanitizer test links them
+    with an instrumented copy of the host API."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(UNITS)) as pool:
+        objs = list(pool.map(lambda u: _compile(u, OBJ_DIR), UNITS))
+    tmp_lib = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp_lib, LIB_PATH)
     if verbose:
         print("built", LIB_PATH)
     return LIB_PATH
