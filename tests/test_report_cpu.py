@@ -26,7 +26,12 @@ def _detail():
                                                 "copy_gbs": 5600.0},
             "kernels": {"fp16_4096": kern(256, 256, 64, 8, 2, 128.0, 32.0, 4.0, 131072, 256, 239, 1),
                         "int8_4096": kern(256, 256, 128, 8, 2, 256.0, 32.0, 4.0, 131072, 256, 247, 1),
-                        "fp16_skinny": kern(64, 64, 64, 4, 4, 32.0, 128.0, 1.0, 65536, 256, 48, 2)}}
+                        "fp16_skinny": kern(64, 64, 64, 4, 4, 32.0, 128.0, 1.0, 65536, 256, 48, 2),
+                        "int8_256": kern(64, 64, 128, 4, 4, 64.0, 128.0, 1.0, 65536, 16, 68, 2),
+                        "fp16_1024": kern(64, 64, 64, 4, 4, 32.0, 128.0, 1.0, 65536, 256, 68, 2)},
+            # the small configurations are timed per call and from HIP graphs
+            "variants": {"int8_256": {"pipelined": {"us": 5.3}, "graph": {"pipelined": {"us": 3.1}}},
+                         "fp16_1024": {"pipelined": {"us": 7.0}, "graph": {"pipelined": {"us": 6.8}}}}}
 
 
 def test_report_has_every_section(tmp_path):
@@ -39,11 +44,12 @@ def test_report_has_every_section(tmp_path):
         if f.startswith("gemm_"):
             (out / f).write_text(open(os.path.join(profiles, f)).read())
     assert report.main([str(det), str(out)]) == 0
-    for wl in ("fp16_4096", "int8_4096", "fp16_skinny"):
+    for wl in ("fp16_4096", "int8_4096", "fp16_skinny", "int8_256", "fp16_1024"):
         text = (out / ("report_%s.md" % wl)).read_text()
         for section in ("## Baseline", "## Roofline classification", "## Occupancy", "## Compute / load ratio",
                         "## Instruction mix", "## LDS cliff", "## Recommended optimizations"):
             assert section in text, (wl, section)
-        bound = "memory-bound" if wl == "fp16_skinny" else "compute-bound"
-        assert bound in text
+        bound = {"fp16_skinny": "memory-bound", "int8_256": "latency-bound",
+                 "fp16_1024": "latency-bound"}.get(wl, "compute-bound")
+        assert "**%s**" % bound in text, (wl, bound)
         assert "1. " in text.split("## Recommended optimizations")[1]

@@ -17,7 +17,9 @@ Inputs, and nothing else:
 
     python -m tiled_dense_gemm_loop_amd.report DETAIL.json [profiles_dir]
 
-writes ``profiles/report_<workload>.md`` for the metric's three workloads.
+writes ``profiles/report_<workload>.md`` for the metric's three workloads and
+the two small configurations (INT8 256^3, FP16 1024^3), which sit far above
+both roofline floors and are classified as latency-bound.
 """
 from __future__ import annotations
 
@@ -35,7 +37,12 @@ WORKLOADS = {
     "fp16_4096": ("FP16 -> FP32", 4096, 4096, 4096, 2, 2500.0, "TFLOP/s", 4096),
     "int8_4096": ("INT8 -> INT32", 4096, 4096, 4096, 1, 5000.0, "TOP/s", 8192),
     "fp16_skinny": ("FP16 -> FP32", 16384, 64, 8192, 2, 2500.0, "TFLOP/s", 4096),
+    "int8_256": ("INT8 -> INT32", 256, 256, 256, 1, 5000.0, "TOP/s", 8192),
+    "fp16_1024": ("FP16 -> FP32", 1024, 1024, 1024, 2, 2500.0, "TFLOP/s", 4096),
 }
+# A product whose time exceeds both roofline floors by this factor is bound
+# by neither: launch, latency, or too little work per compute unit.
+LATENCY_FACTOR = 3.0
 HBM_GBS = 8000.0
 LDS_PER_CU = 160 * 1024
 REGS_PER_LANE = 512          # unified VGPR + AGPR file per SIMD lane
@@ -161,10 +168,53 @@ def recommendations(wl: str, line: dict, part: dict, kern: dict, prof: dict, cei
     return sorted(recs, key=lambda r: -r[0])
 
 
+def latency_recommendations(wl: str, us: float, call_us, kern: dict, prof: dict) -> list:
+    """What holds a product that sits far above both roofline floors, ranked
+    by the share of time each could at most recover."""
+    dtype, M, N, K, es, peak, unit, ops_clk = WORKLOADS[wl]
+    cfg, plan = kern["config"], kern["plan"]
+    recs = []
+    grid = plan["grid"]
+    per_wg = (cfg["bm"] + cfg["bn"]) * K * es
+    # the shorter of the trace's kernel time and the graph-replayed launch
+    kus = min(prof.get("kernel_us") or us, us)
+    rate = per_wg / (kus * 1e-6) / (CLOCK_GHZ * 1e9)
+    if grid < NUM_CU:
+        recs.append((1.0 - grid / float(NUM_CU),
+                     "Compute units: %d workgroups of %dx%d for %d CUs, so %.0f%% of the chip works.  K = %d is "
+                     "%d K tile(s), too few to split over more workgroups (split K keeps at least two K tiles "
+                     "per part); the product is as wide as its tiles allow." % (
+                         grid, cfg["bm"], cfg["bn"], NUM_CU, 100.0 * grid / NUM_CU, K, plan["num_tiles"])))
+    else:
+        recs.append((1.0 - min(1.0, rate / plan["need_bytes_per_clk"]),
+                     "L2 -> LDS fill per CU: each workgroup copies %.0f KiB (its A and B panels), %.1f B per "
+                     "clock at %.1f GHz over %.2f us, against the %.0f B per clock a %dx%d tile "
+                     "needs to keep the matrix cores busy.  %d workgroups fill the %d CUs once, and no tile "
+                     "gives every CU work with fewer bytes; split K over larger tiles halves the bytes per CU "
+                     "but adds a summation pass (gemm_*_splitk, when its plan predicts a gain)." % (
+                         per_wg / 1024.0, rate, CLOCK_GHZ, kus, plan["need_bytes_per_clk"], cfg["bm"], cfg["bn"],
+                         grid, NUM_CU)))
+    if call_us and call_us > us:
+        recs.append(((call_us - us) / call_us,
+                     "Launch: a call through the Python binding takes %.2f us against %.2f us per launch replayed "
+                     "from a HIP graph; the difference is host time per call.  Capture repeated calls in a graph "
+                     "(the library records into a capturing stream like any HIP call)." % (call_us, us)))
+    floor = 2.0 * M * N * K / (peak * 1e12) * 1e6
+    recs.append((0.0, "The matrix cores' share is %.2f us of the %.2f us (%.0f%%): nothing on the MFMA side is "
+                      "worth changing at this size." % (floor, us, 100.0 * floor / us)))
+    return sorted(recs, key=lambda r: -r[0])
+
+
 def report(wl: str, detail: dict, profiles: str) -> str:
     dtype, M, N, K, es, peak, unit, ops_clk = WORKLOADS[wl]
     line = detail["line"]
     part = (line.get("metric_parts") or {}).get(wl) or {}
+    call_us = None
+    var = (detail.get("variants") or {}).get(wl) or {}
+    if not part and var.get("graph", {}).get("pipelined"):
+        # the small configurations: kernel-bound time from HIP-graph replays
+        part = {"us": var["graph"]["pipelined"]["us"]}
+        call_us = (var.get("pipelined") or {}).get("us")
     kern = detail["kernels"][wl]
     cfg, plan, res = kern["config"], kern["plan"], kern.get("resources")
     prof = read_profile(profiles, wl)
@@ -186,19 +236,31 @@ def report(wl: str, detail: dict, profiles: str) -> str:
     L += ["## Baseline", "",
           "- Problem: M = %d, N = %d, K = %d, %s; %d operations, %d algorithmic bytes (A and B read once, C written once)." % (
               M, N, K, dtype, ops, alg)]
-    if us:
+    if us and call_us is None:
         L.append("- Time per launch (HIP events, back-to-back launches): %.2f us -> %.1f %s, %.1f GB/s algorithmic." % (
             us, ops / (us * 1e-6) / 1e12, unit, alg / (us * 1e-6) / 1e9))
+    elif us:
+        L.append("- Time per launch replayed from HIP graphs (20 launches per graph): %.2f us -> %.1f %s, %.1f GB/s "
+                 "algorithmic." % (us, ops / (us * 1e-6) / 1e12, unit, alg / (us * 1e-6) / 1e9))
+        if call_us:
+            L.append("- Time per call through the binding (HIP events, back-to-back calls): %.2f us." % call_us)
     if kus:
         L.append("- Kernel time in the rocprofv3 trace of the timed launches: %.2f us -> %.1f %s." % (
             kus, ops / (kus * 1e-6) / 1e12, unit))
     # Roofline
     bound = "memory" if ai < balance else "compute"
+    t_mfma, t_hbm = ops / (peak * 1e12) * 1e6, alg / (HBM_GBS * 1e9) * 1e6
+    if us and us > LATENCY_FACTOR * max(t_mfma, t_hbm):
+        bound = "latency"
     L += ["", "## Roofline classification", "",
           "- Arithmetic intensity: %.1f operations per byte (unique bytes); balance point %.1f (%.0f %s dense / %.0f GB/s)." % (
               ai, balance, peak, unit, HBM_GBS),
           "- Classification: **%s-bound**." % bound]
-    if us:
+    if bound == "latency":
+        L.append("- Floors: %.2f us at the dense peak, %.2f us at HBM's rate; the launch takes %.2f us, %.0fx the "
+                 "larger.  Neither roofline applies: %.1f%% of the %s peak, %.1f%% of HBM." % (
+                     t_mfma, t_hbm, us, us / max(t_mfma, t_hbm), 100 * t_mfma / us, unit, 100 * t_hbm / us))
+    elif us:
         if bound == "compute":
             att = ops / (us * 1e-6) / 1e12 / peak
             L.append("- Attained: %.1f%% of the %.0f %s dense peak." % (100 * att, peak, unit))
@@ -286,7 +348,9 @@ def report(wl: str, detail: dict, profiles: str) -> str:
               max(1, min(per_cu, (res or {}).get("wg_per_cu", per_cu)) * cfg["waves"] // SIMDS))]
     # Recommendations
     L += ["", "## Recommended optimizations (ranked by the share of time each could recover)", ""]
-    for i, (g, text) in enumerate(recommendations(wl, line, part or {"us": us}, kern, prof, ceilings), 1):
+    recs = (latency_recommendations(wl, us, call_us, kern, prof) if bound == "latency"
+            else recommendations(wl, line, part or {"us": us}, kern, prof, ceilings))
+    for i, (g, text) in enumerate(recs, 1):
         L.append("%d. %s" % (i, text))
     return "\n".join(L) + "\n"
 
