@@ -591,7 +591,7 @@ def main():
     detail = {"line": line, "measured_ceilings": ceilings, "launches": launches, "cold": cold,
               "variants": table or None, "transpose_ladder": ladder, "tile_sweep": sweep,
               "kernels": {name: kernel_record(tdg, si.WORKLOADS[name])
-                          for name in PART_NAMES + ("int8_256", "fp16_1024")}}
+                          for name in PART_NAMES + ("int8_256", "fp16_1024", "fp32_4096")}}
     if args.detail_out:
         d = os.path.dirname(os.path.abspath(args.detail_out))
         os.makedirs(d, exist_ok=True)

@@ -28,10 +28,12 @@ def _detail():
                         "int8_4096": kern(256, 256, 128, 8, 2, 256.0, 32.0, 4.0, 131072, 256, 247, 1),
                         "fp16_skinny": kern(64, 64, 64, 4, 4, 32.0, 128.0, 1.0, 65536, 256, 48, 2),
                         "int8_256": kern(64, 64, 128, 4, 4, 64.0, 128.0, 1.0, 65536, 16, 68, 2),
-                        "fp16_1024": kern(64, 64, 64, 4, 4, 32.0, 128.0, 1.0, 65536, 256, 68, 2)},
+                        "fp16_1024": kern(64, 64, 64, 4, 4, 32.0, 128.0, 1.0, 65536, 256, 68, 2),
+                        "fp32_4096": kern(256, 256, 32, 8, 2, 64.0, 4.0, 4.0, 131072, 256, 200, 1)},
             # the small configurations are timed per call and from HIP graphs
             "variants": {"int8_256": {"pipelined": {"us": 5.3}, "graph": {"pipelined": {"us": 3.1}}},
-                         "fp16_1024": {"pipelined": {"us": 7.0}, "graph": {"pipelined": {"us": 6.8}}}}}
+                         "fp16_1024": {"pipelined": {"us": 7.0}, "graph": {"pipelined": {"us": 6.8}}},
+                         "fp32_4096": {"pipelined": {"us": 921.0}}}}
 
 
 def test_report_has_every_section(tmp_path):
@@ -44,7 +46,7 @@ def test_report_has_every_section(tmp_path):
         if f.startswith("gemm_"):
             (out / f).write_text(open(os.path.join(profiles, f)).read())
     assert report.main([str(det), str(out)]) == 0
-    for wl in ("fp16_4096", "int8_4096", "fp16_skinny", "int8_256", "fp16_1024"):
+    for wl in ("fp16_4096", "int8_4096", "fp16_skinny", "int8_256", "fp16_1024", "fp32_4096"):
         text = (out / ("report_%s.md" % wl)).read_text()
         for section in ("## Baseline", "## Roofline classification", "## Occupancy", "## Compute / load ratio",
                         "## Instruction mix", "## LDS cliff", "## Recommended optimizations"):

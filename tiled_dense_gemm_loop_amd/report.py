@@ -17,9 +17,10 @@ Inputs, and nothing else:
 
     python -m tiled_dense_gemm_loop_amd.report DETAIL.json [profiles_dir]
 
-writes ``profiles/report_<workload>.md`` for the metric's three workloads and
-the two small configurations (INT8 256^3, FP16 1024^3), which sit far above
-both roofline floors and are classified as latency-bound.
+writes ``profiles/report_<workload>.md`` for the metric's three workloads,
+FP32 4096^3, and the two small configurations (INT8 256^3, FP16 1024^3),
+which sit far above both roofline floors and are classified as
+latency-bound.
 """
 from __future__ import annotations
 
@@ -39,7 +40,10 @@ WORKLOADS = {
     "fp16_skinny": ("FP16 -> FP32", 16384, 64, 8192, 2, 2500.0, "TFLOP/s", 4096),
     "int8_256": ("INT8 -> INT32", 256, 256, 256, 1, 5000.0, "TOP/s", 8192),
     "fp16_1024": ("FP16 -> FP32", 1024, 1024, 1024, 2, 2500.0, "TFLOP/s", 4096),
+    "fp32_4096": ("FP32 -> FP32", 4096, 4096, 4096, 4, 157.3, "TFLOP/s", 256),
 }
+# The measured MFMA-only ceiling of each compute-bound workload's instruction.
+CEILING_KEY = {"fp16_4096": "mfma_f16_tflops", "int8_4096": "mfma_i8_tops", "fp32_4096": "mfma_f32_tflops"}
 # A product whose time exceeds both roofline floors by this factor is bound
 # by neither: launch, latency, or too little work per compute unit.
 LATENCY_FACTOR = 3.0
@@ -132,7 +136,7 @@ def recommendations(wl: str, line: dict, part: dict, kern: dict, prof: dict, cei
                           "(fetched %.2fx A + B)." % (N, prof.get("refetch", float("nan")))))
         return sorted(recs, key=lambda r: -r[0])
     # compute side
-    ceiling_key = {"fp16_4096": "mfma_f16_tflops", "int8_4096": "mfma_i8_tops"}.get(wl)
+    ceiling_key = CEILING_KEY.get(wl)
     ceil = ceilings.get(ceiling_key) if ceiling_key else None
     achieved = 2.0 * M * N * K / (us * 1e-6) / 1e12
     util = prof.get("mfma_util")
@@ -158,10 +162,12 @@ def recommendations(wl: str, line: dict, part: dict, kern: dict, prof: dict, cei
                                                                                100 * c_share, t_c, 100 * t_c / us)))
     if ceil:
         gain = max(0.0, 1.0 - achieved / ceil)
-        recs.append((gain * 0.5, "Clock: the MFMA-only probe sustains %.0f %s on this box (random operands, the "
-                                 "power limit holds the clock near 1.5-1.7 GHz); the GEMM reaches %.0f%% of it.  "
-                                 "Fewer bytes moved per operation (LDS reads, L2 traffic) leave more of the power "
-                                 "budget to the matrix cores." % (ceil, unit, 100 * achieved / ceil)))
+        recs.append((gain * 0.5, "Clock: the MFMA-only probe sustains %.0f %s on this box with random operands, "
+                                 "%.0f%% of the dense peak, i.e. about %.2f GHz of the %.1f GHz the peak assumes "
+                                 "(the power limit); the GEMM reaches %.0f%% of it.  Fewer bytes moved per "
+                                 "operation (LDS reads, L2 traffic) leave more of the power budget to the matrix "
+                                 "cores." % (ceil, unit, 100 * ceil / peak, CLOCK_GHZ * ceil / peak, CLOCK_GHZ,
+                                             100 * achieved / ceil)))
     if kern["config"]["variant"] != 3:
         recs.append((0.05, "Use the direct-to-LDS loop: the register-prefetch loop's drain costs LDS write "
                            "bandwidth and registers."))
@@ -215,6 +221,9 @@ def report(wl: str, detail: dict, profiles: str) -> str:
         # the small configurations: kernel-bound time from HIP-graph replays
         part = {"us": var["graph"]["pipelined"]["us"]}
         call_us = (var.get("pipelined") or {}).get("us")
+    elif not part and var.get("pipelined"):
+        # a long product outside the metric: its back-to-back launches
+        part = {"us": var["pipelined"]["us"]}
     kern = detail["kernels"][wl]
     cfg, plan, res = kern["config"], kern["plan"], kern.get("resources")
     prof = read_profile(profiles, wl)
@@ -264,7 +273,7 @@ def report(wl: str, detail: dict, profiles: str) -> str:
         if bound == "compute":
             att = ops / (us * 1e-6) / 1e12 / peak
             L.append("- Attained: %.1f%% of the %.0f %s dense peak." % (100 * att, peak, unit))
-            ck = {"fp16_4096": "mfma_f16_tflops", "int8_4096": "mfma_i8_tops"}.get(wl)
+            ck = CEILING_KEY.get(wl)
             if ck and ceilings.get(ck):
                 L.append("- Against the measured MFMA-only ceiling of this box (%.0f %s): %.1f%%." % (
                     ceilings[ck], unit, 100 * ops / (us * 1e-6) / 1e12 / ceilings[ck]))
@@ -313,11 +322,15 @@ def report(wl: str, detail: dict, profiles: str) -> str:
         w = prof["waves"]
         L += ["", "## Instruction mix (rocprofv3 SQ instruction counters, per wave)", "",
               "| instruction | count per wave | note |", "|---|---|---|"]
+        mfma_note = ("four 32x32x2 MFMAs per 32x32 block per K step of 32 bytes" if es == 4
+                     else "one 32x32 block per K step of 32 bytes")
+        lds_note = ("fragment reads (`ds_read_b128` for A, four `ds_read_b32` per B fragment)" if es == 4
+                    else "fragment reads (`ds_read_b128`, transposing `ds_read_b64_tr`)")
         if "mfma" in prof:
-            L.append("| MFMA | %.0f | one 32x32 block per K step of 32 bytes |" % (prof["mfma"] / w))
+            L.append("| MFMA | %.0f | %s |" % (prof["mfma"] / w, mfma_note))
         L.append("| vector-memory reads | %.0f | 16-byte LDS DMA (`global_load_lds_dwordx4`) |" % (prof.get("vmem_rd", 0) / w))
         L.append("| vector-memory writes | %.0f | C stores, 4 bytes per lane |" % (prof.get("vmem_wr", 0) / w))
-        L.append("| LDS | %.0f | fragment reads (`ds_read_b128`, transposing `ds_read_b64_tr`) |" % (prof.get("lds", 0) / w))
+        L.append("| LDS | %.0f | %s |" % (prof.get("lds", 0) / w, lds_note))
         L.append("| VALU (non-MFMA) | %.0f | addresses, selects |" % (prof.get("valu", 0) / w))
         L.append("| SALU | %.0f | loop control, wave-uniform bases |" % (prof.get("salu", 0) / w))
         if prof.get("lds_active"):
