@@ -834,14 +834,29 @@ def test_k_split_additivity(lib):
         assert torch.equal(full, part)
 
 
-def test_repeat_runs_are_bitwise_identical(lib):
+@pytest.mark.parametrize("name,launches", [("fp16_1024", 10), ("fp16_4096", 60), ("int8_4096", 60),
+                                           ("fp16_skinny", 60)])
+def test_repeat_runs_are_bitwise_identical(lib, name, launches):
+    """The benchmark's workloads launched one after another with no host
+    wait between them, into alternating outputs: every launch equals the
+    first bit for bit (compared on the device, in stream order).  A missing
+    wait or barrier in the K loop lets a launch read a tile before it lands,
+    and shows up here as a launch that differs."""
     import torch
-    wl = si.WORKLOADS["fp16_1024"]
+    wl = si.WORKLOADS[name]
     A, B = wl.operands()
     dA, dB = to_device(A), to_device(B)
-    first = gemm(lib, F16, "pipelined", dA, dB)
-    for _ in range(10):
-        assert torch.equal(first, gemm(lib, F16, "pipelined", dA, dB))
+    dt = I8 if wl.dtype == "i8" else F16
+    first = gemm(lib, dt, "pipelined", dA, dB)
+    outs = [torch.empty_like(first) for _ in range(2)]
+    differs = []
+    for i in range(launches):
+        C = outs[i % 2]
+        C.fill_(-1)
+        gemm(lib, dt, "pipelined", dA, dB, C)
+        differs.append(torch.ne(C, first).any())
+    bad = [i for i, d in enumerate(differs) if bool(d)]
+    assert not bad, (name, bad)
 
 
 def test_concurrent_streams_from_host_threads(lib):
