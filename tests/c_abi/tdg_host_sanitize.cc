@@ -262,6 +262,15 @@ void invalid_calls() {
         for (int rc : rcs) EXPECT(rc == TDG_ERR_INVALID_ARG, "invalid call returned %d", rc);
     }
     EXPECT(gemm_splitk_noalloc(9, 4, 4, 4, A, 4, B, 4, C, 4, 0, nullptr) == TDG_ERR_INVALID_ARG, "noalloc dtype");
+    // parts * M * N * 4 past 64 bits must not wrap into a size that fits
+    for (int parts : {1 << 28, (1 << 28) + 1, 0x7FFFFFFF}) {
+        const int64_t M = 1 << 17, N = 1 << 17, K = 1024;
+        void *W = (void *)((uintptr_t)1 << 45);
+        EXPECT(gemm_f16f32_splitk(M, N, K, (const uint16_t *)A, K, (const uint16_t *)B, N, (float *)C, N, parts, W,
+                                  16, nullptr) == TDG_ERR_INVALID_ARG, "wrapped workspace size, %d parts", parts);
+        EXPECT(gemm_splitk_noalloc(TDG_DTYPE_F16F32, M, N, K, A, K, B, N, C, N, parts, nullptr) == TDG_ERR_SCRATCH,
+               "wrapped scratch size, %d parts", parts);
+    }
     EXPECT(gemm_f16f32_splitk(4, 4, 4, (const uint16_t *)A, 4, (const uint16_t *)B, 4, (float *)C, 4, -1,
                               nullptr, 0, nullptr) == TDG_ERR_INVALID_ARG, "negative parts");
     EXPECT(tdg_copy_f32(-1, 4, (const float *)A, 4, (float *)C, 4, nullptr) == TDG_ERR_INVALID_ARG, "copy rows");

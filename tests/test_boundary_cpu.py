@@ -503,6 +503,27 @@ def test_splitk_plan_and_workspace_validation():
     assert call(None, 0, parts=1) == tdg.TDG_ERR_NO_DEVICE    # one part needs no workspace
 
 
+@no_device_only
+def test_split_k_workspace_size_does_not_wrap():
+    """A caller's part count times M * N * 4 can exceed 64 bits for outputs
+    that fit in device memory (C of 131072^2 floats is 64 GB; 2^28 parts
+    make the product exactly 2^64).  The size must not wrap to a small
+    number that a short workspace or the built-in scratch array passes:
+    both entry points refuse the call before any HIP call."""
+    lib = tdg.load_library()
+    M = N = 1 << 17
+    K = 1024
+    A, B, C, W = 1 << 40, 1 << 41, 1 << 42, 1 << 45
+    for parts in (1 << 28, (1 << 28) + 1, (1 << 31) - 1):
+        assert lib.gemm_f16f32_splitk(M, N, K, A, K, B, N, C, N, parts, W, 16, None) == \
+            tdg.TDG_ERR_INVALID_ARG, parts
+        assert lib.gemm_splitk_noalloc(tdg.TDG_DTYPE_F16F32, M, N, K, A, K, B, N, C, N, parts, None) == \
+            tdg.TDG_ERR_SCRATCH, parts
+    # a workspace of the exact size is accepted (the call gets to the device check)
+    assert lib.gemm_f16f32_splitk(256, 256, 8192, A, 8192, B, 256, C, 256, 4, W, 4 * 256 * 256 * 4,
+                                  None) == tdg.TDG_ERR_NO_DEVICE
+
+
 def test_sizes_keep_a_margin_below_2_31():
     """The kernels form tile start + tile extent in 32 bits, so M, N and K
     stop 2^16 short of 2^31: planning M at the limit works (a dense N or K

@@ -757,7 +757,7 @@ int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, i
             if (p > 1 && k_tiles < 2 * p) break;
             const int64_t per = ceil_div(k_tiles, p);
             const int64_t used = ceil_div(k_tiles, per);
-            if (used > 1 && (uint64_t)used * (uint64_t)M * (uint64_t)N * 4u > ws_limit) continue;
+            if (used > 1 && tdg::splitk_bytes(used, M, N) > ws_limit) continue;
             double t = predict_us(r, fig.wg_per_cu, fig.grid * used, per * bk);
             if (used > 1) t += sum_parts_us((int)used, M, N);
             if (best_t < 0.0 || t < best_t) {
@@ -797,6 +797,13 @@ int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, i
 
 namespace tdg {
 
+uint64_t splitk_bytes(int64_t parts, int64_t M, int64_t N) {
+    if (parts <= 0 || M <= 0 || N <= 0) return 0;
+    const uint64_t one = (uint64_t)M * (uint64_t)N * 4u;
+    if (one > UINT64_MAX / (uint64_t)parts) return UINT64_MAX;
+    return one * (uint64_t)parts;
+}
+
 int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                   int64_t ldb, const void *C, int64_t ldc) {
     return validate(dtype, M, N, K, A, lda, B, ldb, C, ldc);
@@ -818,8 +825,8 @@ int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_
         return run(dtype, M, N, K, A, lda, B, ldb, C, ldc, stream, parts <= 1 && cfg.bm ? &cfg : nullptr,
                    true);
     // The workspace: parts dense M x N partial products, 16-byte aligned,
-    // apart from A, B and C.
-    const uint64_t need = (uint64_t)parts * (uint64_t)M * (uint64_t)N * 4u;
+    // apart from A, B and C (a size past 64 bits fits no workspace).
+    const uint64_t need = splitk_bytes(parts, M, N);
     if (!ws || ws_bytes < need || (uintptr_t)ws % 16) return TDG_ERR_INVALID_ARG;
     const int es = elem_size(dtype);
     if (ranges_overlap((uintptr_t)ws, need, (uintptr_t)A, span_bytes(M, K, lda, es)) ||
@@ -983,7 +990,7 @@ int tdg_splitk_plan(int dtype, int64_t M, int64_t N, int64_t K, int *parts, size
     tdg_config cfg;
     const int rc = splitk_choose(dtype, M, N, K, &cfg, parts);
     if (rc != TDG_OK) return rc;
-    if (workspace_bytes && *parts > 1) *workspace_bytes = (size_t)*parts * (size_t)M * (size_t)N * 4u;
+    if (workspace_bytes && *parts > 1) *workspace_bytes = (size_t)tdg::splitk_bytes(*parts, M, N);
     return TDG_OK;
 }
 

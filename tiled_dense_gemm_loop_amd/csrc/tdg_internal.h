@@ -35,6 +35,11 @@ int device_check();
 int launch_sum_parts(int dtype, int parts, const void *ws, int64_t M, int64_t N, void *C, int64_t ldc,
                      void *stream);
 
+// Bytes of `parts` dense M x N partial products of 4 bytes, or UINT64_MAX
+// when that does not fit in 64 bits (0 <= M, N < 2^31, so one product's
+// M * N * 4 always does; a caller's part count can still carry it over).
+uint64_t splitk_bytes(int64_t parts, int64_t M, int64_t N);
+
 // Argument validation of a GEMM call (TDG_OK or TDG_ERR_INVALID_ARG); no
 // HIP call.
 int validate_gemm(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,

@@ -58,7 +58,7 @@ extern "C" int gemm_splitk_noalloc(int dtype, int64_t M, int64_t N, int64_t K, c
     int rc = tdg::validate_gemm(dtype, M, N, K, A, lda, B, ldb, C, ldc);
     if (rc != TDG_OK) return rc;
     if (parts < 0) return TDG_ERR_INVALID_ARG;
-    if (parts > 1 && (uint64_t)parts * (uint64_t)M * (uint64_t)N * 4u > (uint64_t)TDG_NOALLOC_SCRATCH_BYTES)
+    if (parts > 1 && tdg::splitk_bytes(parts, M, N) > (uint64_t)TDG_NOALLOC_SCRATCH_BYTES)
         return TDG_ERR_SCRATCH;
     if (M == 0 || N == 0) return TDG_OK;
     rc = tdg::device_check();
