@@ -515,13 +515,32 @@ def test_split_k_workspace_size_does_not_wrap():
     K = 1024
     A, B, C, W = 1 << 40, 1 << 41, 1 << 42, 1 << 45
     for parts in (1 << 28, (1 << 28) + 1, (1 << 31) - 1):
-        assert lib.gemm_f16f32_splitk(M, N, K, A, K, B, N, C, N, parts, W, 16, None) == \
-            tdg.TDG_ERR_INVALID_ARG, parts
+        for claimed in (16, (1 << 64) - 1):     # no workspace holds 2^64 bytes, whatever is claimed
+            assert lib.gemm_f16f32_splitk(M, N, K, A, K, B, N, C, N, parts, W, claimed, None) == \
+                tdg.TDG_ERR_INVALID_ARG, (parts, claimed)
         assert lib.gemm_splitk_noalloc(tdg.TDG_DTYPE_F16F32, M, N, K, A, K, B, N, C, N, parts, None) == \
             tdg.TDG_ERR_SCRATCH, parts
     # a workspace of the exact size is accepted (the call gets to the device check)
     assert lib.gemm_f16f32_splitk(256, 256, 8192, A, 8192, B, 256, C, 256, 4, W, 4 * 256 * 256 * 4,
                                   None) == tdg.TDG_ERR_NO_DEVICE
+
+
+@no_device_only
+def test_split_k_with_an_empty_k_plans_nothing():
+    """K = 0 is a valid product (C is zero-filled).  Asked to choose the part
+    count (parts = 0), both split-K entry points must not plan a split of
+    zero K tiles (that divided by zero in the host process): the call goes
+    on to the plain zero fill and reaches the device check here."""
+    lib = tdg.load_library()
+    A, B, C, W = 1 << 40, 1 << 41, 1 << 42, 1 << 45
+    for M, N in ((64, 1), (256, 256), (1, 4096)):
+        for fn in (lib.gemm_f16f32_splitk, lib.gemm_i8i32_splitk, lib.gemm_f32f32_splitk):
+            assert fn(M, N, 0, None, 1, None, N, C, N, 0, None, 0, None) == tdg.TDG_ERR_NO_DEVICE
+            assert fn(M, N, 0, A, 1, B, N, C, N, 0, W, 16, None) == tdg.TDG_ERR_NO_DEVICE
+        for dt in (0, 1, 2):
+            assert lib.gemm_splitk_noalloc(dt, M, N, 0, None, 1, None, N, C, N, 0, None) == \
+                tdg.TDG_ERR_NO_DEVICE
+    assert tdg.tdg_splitk_plan(tdg.TDG_DTYPE_F16F32, 256, 256, 0) == (1, 0)
 
 
 def test_sizes_keep_a_margin_below_2_31():

@@ -953,6 +953,30 @@ def test_split_k(lib, dtype, M, N, K, parts):
     assert torch.equal(C1, C2)
 
 
+@pytest.mark.parametrize("dtype", [F16, I8, F32])
+def test_split_k_with_an_empty_k_zero_fills(lib, dtype):
+    """K = 0 through the split-K entry points with the part count left to
+    the planner (parts = 0, straight through the C ABI) and through the
+    allocation-free one: C is all zeros."""
+    import torch
+    lib_c = lib.load_library()
+    out_t = torch.int32 if dtype == I8 else torch.float32
+    raw = {F16: lib_c.gemm_f16f32_splitk, I8: lib_c.gemm_i8i32_splitk, F32: lib_c.gemm_f32f32_splitk}[dtype]
+    in_t = {F16: torch.float16, I8: torch.int8, F32: torch.float32}[dtype]
+    for M, N in ((64, 1), (300, 260)):
+        C = torch.full((M, N), 7, dtype=out_t, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        assert raw(M, N, 0, None, 1, None, N, C.data_ptr(), N, 0, None, 0, stream) == lib.TDG_OK
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(C).item() == 0, (M, N)
+        C.fill_(7)
+        A = torch.empty((M, 0), dtype=in_t, device="cuda")
+        B = torch.empty((0, N), dtype=in_t, device="cuda")
+        lib.gemm_splitk_noalloc(A, B, C, parts=0)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(C).item() == 0, (M, N)
+
+
 def test_split_k_strided_output_and_explicit_workspace(lib):
     """Split K into a strided C view, through a caller-given workspace with
     room to spare; C's padding stays untouched."""

@@ -741,6 +741,9 @@ int splitk_choose(int dtype, int64_t M, int64_t N, int64_t K, tdg_config *cfg, i
                   uint64_t ws_limit = UINT64_MAX) {
     tdg_config req;
     memset(&req, 0, sizeof(req));
+    memset(cfg, 0, sizeof(*cfg));
+    *parts = 1;
+    if (M <= 0 || N <= 0 || K <= 0) return TDG_OK;  // nothing to split
     const Choice base = choose_config(dtype, M, N, K, req);
     if (!base.tile) return TDG_ERR_UNSUPPORTED;
     const int es = elem_size(dtype);
@@ -817,7 +820,8 @@ int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_
     if (parts < 0) return TDG_ERR_INVALID_ARG;
     tdg_config cfg;
     memset(&cfg, 0, sizeof(cfg));
-    if (parts == 0) {
+    // An empty product (K == 0: C is zero-filled) has nothing to split.
+    if (parts == 0 && M > 0 && N > 0 && K > 0) {
         rc = splitk_choose(dtype, M, N, K, &cfg, &parts, auto_limit);
         if (rc != TDG_OK) return rc;
     }
@@ -827,7 +831,7 @@ int run_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_
     // The workspace: parts dense M x N partial products, 16-byte aligned,
     // apart from A, B and C (a size past 64 bits fits no workspace).
     const uint64_t need = splitk_bytes(parts, M, N);
-    if (!ws || ws_bytes < need || (uintptr_t)ws % 16) return TDG_ERR_INVALID_ARG;
+    if (!ws || need == UINT64_MAX || ws_bytes < need || (uintptr_t)ws % 16) return TDG_ERR_INVALID_ARG;
     const int es = elem_size(dtype);
     if (ranges_overlap((uintptr_t)ws, need, (uintptr_t)A, span_bytes(M, K, lda, es)) ||
         ranges_overlap((uintptr_t)ws, need, (uintptr_t)B, span_bytes(K, N, ldb, es)) ||
