@@ -294,8 +294,9 @@ int tdg_predict_us(int dtype, int bm, int bn, int waves, int stages, int64_t M, 
  * wave-slot and register limits; "Analyze Kernel Bottleneck", Step 3 and
  * Step 6), and num_tiles / grid for an M x N x K product.  bk is in
  * elements; variant only affects the register estimate (register staging).
- * Host-only; returns TDG_ERR_INVALID_ARG for non-positive tile sizes or
- * waves, stages outside 1..8, or negative M, N, K. */
+ * Host-only; returns TDG_ERR_INVALID_ARG for tile sizes outside 1..65536,
+ * waves outside 1..16, stages outside 1..8, or M, N, K outside the range
+ * every entry point accepts (0 .. 2^31 - 2^16). */
 int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, int variant,
                      int64_t M, int64_t N, int64_t K, tdg_plan_info *info);
 

@@ -229,6 +229,49 @@ void figures_sweep() {
     EXPECT(tdg_set_debug_flags(8) == TDG_ERR_INVALID_ARG, "unknown debug bit");
 }
 
+// Random and extreme arguments for every host-only entry point: whatever
+// they are, the calls return a status, and the sanitizers see no undefined
+// arithmetic on the way.
+void extreme_fuzz() {
+    const int64_t v64[] = {0, 1, -1, 2, 63, 64, 65, 255, 256, 257, 4095, 4096, 4097, 65535, 65536, 65537,
+                           (int64_t)1 << 20, kMaxDim - 1, kMaxDim, kMaxDim + 1, (int64_t)1 << 32, (int64_t)1 << 40,
+                           INT64_MAX, INT64_MIN, INT32_MAX, INT32_MIN};
+    const int nv = sizeof(v64) / sizeof(v64[0]);
+    auto any64 = [&]() { return (next_u64() & 1) ? v64[next_u64() % nv] : (int64_t)(next_u64() % 100000); };
+    auto any32 = [&]() {
+        const int64_t v = any64();
+        return (int)(v > INT32_MAX ? INT32_MAX : v < INT32_MIN ? INT32_MIN : v);
+    };
+    for (int it = 0; it < 60000; it++) {
+        const int dtype = (int)(next_u64() % 5) - 1;
+        tdg_plan_info info;
+        tdg_config c;
+        std::memset(&c, 0, sizeof(c));
+        if (next_u64() & 1) {
+            c.bm = any32(); c.bn = any32(); c.bk = any32(); c.waves = any32();
+            c.lds_stages = any32(); c.variant = any32();
+        }
+        int rc = tdg_plan(dtype, any64(), any64(), any64(), &c, &info);
+        EXPECT(status_known(rc), "plan status %d", rc);
+        std::memset(&c, 0, sizeof(c));
+        rc = tdg_plan_operands(dtype, any64(), any64(), any64(), (const void *)(uintptr_t)next_u64(), any64(),
+                               (const void *)(uintptr_t)next_u64(), any64(), &c, &info);
+        EXPECT(status_known(rc), "plan_operands status %d", rc);
+        rc = tdg_tile_figures(dtype, any32(), any32(), any32(), any32(), any32(), any32(), any64(), any64(), any64(),
+                              &info);
+        EXPECT(status_known(rc), "figures status %d", rc);
+        double us;
+        rc = tdg_predict_us(dtype, any32(), any32(), any32(), any32(), any64(), any64(), any64(), &us);
+        EXPECT(status_known(rc), "predict status %d", rc);
+        int parts;
+        size_t ws;
+        rc = tdg_splitk_plan(dtype, any64(), any64(), any64(), &parts, &ws);
+        EXPECT(status_known(rc), "splitk_plan status %d", rc);
+        (void)tdg_mfma_probe_ops(dtype, any64());
+        (void)tdg_lds_probe_bytes(dtype, any64());
+    }
+}
+
 // Arguments every entry point must reject before any HIP call.
 void invalid_calls() {
     const uintptr_t a = (uintptr_t)1 << 40, b = a + ((uintptr_t)1 << 36), c = a + ((uintptr_t)1 << 38);
@@ -315,11 +358,13 @@ void valid_calls_without_device(int thread) {
 }  // namespace
 
 int main() {
+    if (const char *seed = std::getenv("TDG_FUZZ_SEED")) g_rng ^= std::strtoull(seed, nullptr, 10) * 0x9E3779B97F4A7C15ull;
     int devices = 0;
     const bool no_device = hipGetDeviceCount(&devices) != hipSuccess || devices == 0;
     planner_sweep();
     operands_sweep();
     figures_sweep();
+    extreme_fuzz();
     invalid_calls();
     std::vector<std::thread> pool;
     for (int t = 0; t < 8; t++)

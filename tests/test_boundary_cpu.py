@@ -211,6 +211,23 @@ def test_lds_budget_matches_the_pages(case):
     assert info["lds_bytes"] == case["lds_bytes"]
 
 
+def test_tile_figures_argument_ranges():
+    """The tile arithmetic takes any tile up to 65536 on a side (its
+    products stay exact) and the sizes every entry point accepts; beyond
+    those, and for non-positive tiles or waves outside 1..16, it refuses."""
+    F16 = tdg.TDG_DTYPE_F16F32
+    lim = (1 << 31) - (1 << 16)
+    big = tdg.tdg_tile_figures(F16, 65536, 65536, 65536, waves=16, stages=8, M=lim, N=lim, K=lim)
+    assert big["lds_bytes"] == 8 * (65536 * 65536 * 2) * 2 and big["wg_per_cu"] == 0
+    assert big["est_regs"] > 512
+    for args, kw in (((F16, 65537, 64, 64), {}), ((F16, 64, 65537, 64), {}), ((F16, 64, 64, 65537), {}),
+                     ((F16, 0, 64, 64), {}), ((F16, 64, 64, 64), {"waves": 17}),
+                     ((F16, 64, 64, 64), {"stages": 9}), ((F16, 64, 64, 64), {"M": lim + 1}),
+                     ((F16, 64, 64, 64), {"K": -1})):
+        with pytest.raises(tdg.TdgError):
+            tdg.tdg_tile_figures(*args, **kw)
+
+
 def test_doubling_doubles():
     for c in GOLDEN["lds_budget"]:
         one = tdg.tdg_tile_figures(DT[c["dtype"]], c["bm"], c["bn"], c["bk"], stages=1)

@@ -212,16 +212,22 @@ bool offsets_fit(const KernelEntry &e, int64_t lda, int64_t ldb) {
     return fits(a_rows, lda, (uint64_t)e.bkb) && fits(b_rows, ldb, (uint64_t)e.bn * es);
 }
 
+// Largest tile side (bm, bn, bk) the tile arithmetic accepts: far beyond any
+// tile that fits the LDS, and small enough for its products to stay exact.
+constexpr int kMaxTileSide = 1 << 16;
+
 // Estimated 32-bit registers per lane: accumulators, register staging of one
-// K tile (not for direct-to-LDS) and two sets of MFMA fragments.
+// K tile (not for direct-to-LDS) and two sets of MFMA fragments.  (64-bit
+// arithmetic: tiles up to kMaxTileSide on a side.)
 int est_regs(int bm, int bn, int bkb, int waves, int variant) {
-    const int lanes = waves * 64;
-    const int acc = bm * bn / lanes;
-    const int staging = variant == TDG_VARIANT_DIRECT_LDS ? 0 : (bm + bn) * bkb / lanes / 4;
+    const int64_t lanes = (int64_t)waves * 64;
+    const int64_t acc = (int64_t)bm * bn / lanes;
+    const int64_t staging = variant == TDG_VARIANT_DIRECT_LDS ? 0 : ((int64_t)bm + bn) * bkb / lanes / 4;
     // a wave owns about (bm * bn / waves) outputs, split into 32x32 blocks
     const double wave_side = 32.0 * __builtin_sqrt((double)bm * bn / waves / 1024.0);
-    const int frags = 2 * 2 * 4 * (int)(wave_side / 32.0 + 0.5);
-    return acc + staging + frags + 24;
+    const int64_t frags = 2 * 2 * 4 * (int64_t)(wave_side / 32.0 + 0.5);
+    const int64_t total = acc + staging + frags + 24;
+    return total > INT32_MAX ? INT32_MAX : (int)total;
 }
 
 // Whether tile rows walk K from their own offsets: when all of B fits in half
@@ -441,7 +447,7 @@ Choice choose_config(int dtype, int64_t M, int64_t N, int64_t K, const tdg_confi
     double best_t = 0.0;
     const int es = elem_size(dtype);
     const bool any_variant_ok = req.variant == TDG_VARIANT_AUTO || req.variant == TDG_VARIANT_DIRECT_LDS;
-    if (req.bk == 0 || req.bk * es == 128) {
+    if (req.bk == 0 || (int64_t)req.bk * es == 128) {
         for (const PerfRow &r : kPerf) {
             if (r.dtype != dtype) continue;
             if ((req.bm && req.bm != r.bm) || (req.bn && req.bn != r.bn) ||
@@ -951,7 +957,8 @@ int tdg_tile_figures(int dtype, int bm, int bn, int bk, int waves, int stages, i
                      int64_t M, int64_t N, int64_t K, tdg_plan_info *info) {
     if (!dtype_ok(dtype)) return TDG_ERR_INVALID_ARG;
     if (bm <= 0 || bn <= 0 || bk <= 0 || waves <= 0 || waves > 16) return TDG_ERR_INVALID_ARG;
-    if (stages < 1 || stages > 8 || M < 0 || N < 0 || K < 0 || !info) return TDG_ERR_INVALID_ARG;
+    if (bm > kMaxTileSide || bn > kMaxTileSide || bk > kMaxTileSide) return TDG_ERR_INVALID_ARG;
+    if (stages < 1 || stages > 8 || !dims_ok(M, N, K) || !info) return TDG_ERR_INVALID_ARG;
     tile_figures(dtype, bm, bn, bk, waves, stages, variant, M, N, K, info);
     return TDG_OK;
 }
