@@ -127,3 +127,37 @@ def test_large_matrix_blocks(lib):
         del out
     del dx
     torch.cuda.empty_cache()
+
+
+def test_random_shapes_strides_and_offsets(lib):
+    """A seeded sweep: random shapes (1..1500, a third near multiples of the
+    64-wide tile), input and output views at element offsets 0..5 with row
+    padding 0..9, every method and the copy, each against the oracle bit for
+    bit; the output's padding stays untouched."""
+    import random
+    import torch
+    rng = random.Random(21)
+    methods = ["copy"] + METHODS + ["auto"]
+    for case in range(60):
+        rows, cols = rng.randint(1, 1500), rng.randint(1, 1500)
+        if rng.random() < 0.3:
+            rows = max(1, rng.choice((64, 128, 256, 1024)) + rng.randint(-2, 2))
+            cols = max(1, rng.choice((64, 128, 256, 1024)) + rng.randint(-2, 2))
+        oi, pi, oo, po = rng.randint(0, 5), rng.randint(0, 9), rng.randint(0, 5), rng.randint(0, 9)
+        big = _bits(rows, cols + oi + pi, 700 + case)
+        x = big[:, oi:oi + cols]
+        dx = _dev(big)[:, oi:oi + cols]
+        m = rng.choice(methods)
+        orows, ocols = (rows, cols) if m == "copy" else (cols, rows)
+        out_big = torch.full((orows, ocols + oo + po), -7.0, dtype=torch.float32, device="cuda")
+        out = out_big[:, oo:oo + ocols]
+        if m == "copy":
+            lib.tdg_copy_f32(dx, out)
+            ref = oracle.copy_u32(x)
+        else:
+            lib.tdg_transpose_f32(dx, out, method=_method(lib, m))
+            ref = oracle.transpose_u32(x)
+        what = (case, rows, cols, oi, pi, oo, po, m)
+        assert np.array_equal(_host(out), ref), what
+        pad = out_big.cpu().numpy()
+        assert np.all(pad[:, :oo] == -7.0) and np.all(pad[:, oo + ocols:] == -7.0), what
