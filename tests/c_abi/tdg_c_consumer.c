@@ -7,9 +7,11 @@
  *                        device is needed, because every check runs before
  *                        any HIP call.
  *   tdg_c_consumer gpu   INT8, FP16 and FP32 products on the device, on a
- *                        ragged shape and a whole-tile one, each checked
- *                        against the CPU oracle (liboracle_gemm.so): INT8
- *                        bit-exact, FP16 and FP32 within 1e-4 * sum |a b|.
+ *                        ragged shape and a whole-tile one, plain, with K
+ *                        split through a workspace and through the
+ *                        allocation-free entry point, each checked against
+ *                        the CPU oracle (liboracle_gemm.so): INT8 bit-exact,
+ *                        FP16 and FP32 within 1e-4 * sum |a b|.
  *
  * Prints one line per check and exits non-zero at the first failure. */
 #include <hip/hip_runtime_api.h>
@@ -181,6 +183,29 @@ static int gpu_case(int dtype, int64_t M, int64_t N, int64_t K) {
             }
         }
         hipFree(ws);
+        /* and through the allocation-free entry point, which needs no
+           workspace at all: 3 parts, then the planner's count */
+        {
+            const int counts[2] = {3, 0};
+            int c;
+            for (c = 0; c < 2; c++) {
+                HIP_OK(hipMemset(dc, 0, nc * 4));
+                rc = gemm_splitk_noalloc(dtype, M, N, K, da, K, db, N, dc, N, counts[c], NULL);
+                CHECK(rc == TDG_OK, "no-alloc split K dtype %d parts %d: %s", dtype, counts[c],
+                      tdg_status_string(rc));
+                HIP_OK(hipDeviceSynchronize());
+                HIP_OK(hipMemcpy(hc, dc, nc * 4, hipMemcpyDeviceToHost));
+                for (i = 0; i < nc; i++) {
+                    if (dtype == TDG_DTYPE_I8I32) {
+                        CHECK((int64_t)((int32_t *)hc)[i] == iref[i], "no-alloc int8 element %zu", i);
+                    } else {
+                        const double got = ((float *)hc)[i];
+                        CHECK(fabs(got - ref[i]) <= 1e-4 * sum[i], "no-alloc element %zu: %.9g vs %.9g", i, got,
+                              ref[i]);
+                    }
+                }
+            }
+        }
     }
     printf("gpu dtype %d %lldx%lldx%lld ok\n", dtype, (long long)M, (long long)N, (long long)K);
     hipFree(da);
