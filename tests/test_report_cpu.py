@@ -55,3 +55,21 @@ def test_report_has_every_section(tmp_path):
                  "fp16_1024": "latency-bound"}.get(wl, "compute-bound")
         assert "**%s**" % bound in text, (wl, bound)
         assert "1. " in text.split("## Recommended optimizations")[1]
+
+
+def test_planner_command_line(capsys):
+    """python -m tiled_dense_gemm_loop_amd.plan prints the planner's choice
+    and its arithmetic for a product, and the form a call on given operands
+    runs; no GPU is needed."""
+    from tiled_dense_gemm_loop_amd import plan
+    assert plan.main(["f16", "4096", "4096", "4096"]) == 0
+    out = capsys.readouterr().out
+    assert "256x256x64 tile, 8 waves, 2 LDS buffer(s), direct_lds" in out
+    assert "ratio: 128.0 operations per byte" in out and "32.0 B per clock" in out
+    assert "K loop: 64 tile(s), pipelined" in out and "split K: not predicted faster" in out
+    assert plan.main(["i8", "256", "256", "65536"]) == 0
+    assert "split K: 32 parts" in capsys.readouterr().out
+    assert plan.main(["f16", "4095", "4095", "4095", "--misalign", "2"]) == 0
+    assert "bounds-checked" in capsys.readouterr().out
+    assert plan.main(["f32", "1", "1", "1"]) == 0
+    assert "not pipelined (one K tile)" in capsys.readouterr().out
