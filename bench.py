@@ -51,15 +51,16 @@ def roofline_bound(ops: float, alg_bytes: float, peak_gops: float, bw_gbs: float
     return "hbm" if ops / alg_bytes < balance_point(peak_gops, bw_gbs) else "mfma"
 
 
-def profiled_traffic(kernel_desc: str):
-    """HBM bytes per launch from a committed rocprofv3 summary in profiles/
-    (calibrated FETCH_SIZE + WRITE_SIZE), or None when no summary matches this
-    kernel configuration and the current kernel source."""
+def profiled_traffic(workload: str, kernel_desc: str):
+    """HBM bytes per launch from the committed rocprofv3 summary of this
+    workload in profiles/ (gemm_<workload>_*.md; calibrated FETCH_SIZE +
+    WRITE_SIZE), or None when no summary of it matches this kernel
+    configuration and the current kernel source."""
     import glob
     import hashlib
     src = os.path.join(ROOT, "tiled_dense_gemm_loop_amd", "csrc", "tdg_kernels.hpp")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "gemm_%s_*.md" % workload))):
         fields = {}
         for line in open(path):
             for key in ("Kernel source sha256[:16]: ", "Config: "):
@@ -513,7 +514,7 @@ def main():
     kernel_desc = "%dx%dx%d tile, %d waves, %d LDS stages, %s" % (
         cfg["bm"], cfg["bn"], cfg["bk"], cfg["waves"], cfg["lds_stages"],
         tdg.VARIANT_NAMES[cfg["variant"]])
-    traffic = profiled_traffic(kernel_desc)
+    traffic = profiled_traffic(wl.name, kernel_desc)
     alg_bytes = (wl.M * wl.K + wl.K * wl.N) * ELEM_BYTES[wl.dtype] + wl.M * wl.N * 4
     bound = roofline_bound(2.0 * wl.M * wl.N * wl.K, alg_bytes, PEAK[wl.dtype] * 1e3,
                            HBM_PEAK_GBS)

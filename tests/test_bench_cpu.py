@@ -44,22 +44,27 @@ def test_throughput_arithmetic():
 def test_profiled_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     """The committed FP16 4096^3 summary gives the headline's traffic for the
     current kernel source; a copy of the tree whose kernel source differs by
-    one byte gets None, as does a configuration no summary covers."""
+    one byte gets None, as does a configuration no summary covers and a
+    workload whose summaries name the same configuration but another
+    product (the ragged 4000^3 runs the same tile)."""
     desc = None
     for line in open(os.path.join(ROOT, "profiles", "gemm_fp16_4096_direct_lds_s2_w8_256x256x64.md")):
         if line.startswith("Config: "):
             desc = line[len("Config: "):].strip()
     assert desc
-    t = bench.profiled_traffic(desc)
+    t = bench.profiled_traffic("fp16_4096", desc)
     assert t is not None and t > 134217728          # at least the algorithmic bytes
-    assert bench.profiled_traffic(desc + " (not built)") is None
+    assert bench.profiled_traffic("fp16_4096", desc + " (not built)") is None
+    ragged = bench.profiled_traffic("fp16_ragged", desc)
+    assert ragged is None or ragged != t
+    assert bench.profiled_traffic("int8_256", desc) is None
     fake = tmp_path / "tree"
     (fake / "tiled_dense_gemm_loop_amd" / "csrc").mkdir(parents=True)
     shutil.copytree(os.path.join(ROOT, "profiles"), fake / "profiles")
     src = open(os.path.join(ROOT, "tiled_dense_gemm_loop_amd", "csrc", "tdg_kernels.hpp"), "rb").read()
     (fake / "tiled_dense_gemm_loop_amd" / "csrc" / "tdg_kernels.hpp").write_bytes(src + b"\n")
     monkeypatch.setattr(bench, "ROOT", str(fake))
-    assert bench.profiled_traffic(desc) is None
+    assert bench.profiled_traffic("fp16_4096", desc) is None
 
 
 def test_oracle_sample_is_bounded_and_whole_rows():
